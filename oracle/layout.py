@@ -1,0 +1,161 @@
+"""Expected logical planes of a Leech block, and an independent unpacker of
+the packed blob written by the expander (oracle; test infrastructure).
+
+Logical record ("LP3", 112 bits per 24-weight block, the size of the served
+record the Tetra summary describes for the earlier kernel, arXiv 2609.35465,
+section 2: each code unfolded at load time into a 112-bit record):
+  cls    16 bits  class id in the canonical order of oracle.leech.classes()
+  sign   24 bits  bit j = [x_j < 0]  (a zero coordinate has sign 0)
+  R0..R2 3 x 24   bit j of R_i = bit i of rank_j, where rank_j is the index of
+                  |x_j| in the class's ascending list of distinct magnitudes
+Decoding: x_j = (1 - 2 sign_j) * mags(cls)[rank_j].  The class is read once
+per block, not per weight (arXiv 2609.02652, related-work paragraph on
+lookup-table kernels: a Leech class is a permutation pattern, not a value).
+
+Logical class table entry (8 bytes, little-endian u64): bytes 0..4 hold the
+ascending distinct magnitudes padded with 0, byte 7 holds m | parity << 7.
+
+Physical blob (the expander's packing; this module re-reads it from the byte
+layout alone).  nb = K // 24 blocks per row, tau = K % 24 tail columns; every
+section starts at a multiple of 256 bytes:
+  table  u64 [302]          the logical class table
+  codes  u32 [R][nb][3]     word w of block (r, k) carries coordinates 8w..8w+7
+  cls    u16 [R][nb]
+  scale  fp16 [R]
+  tail   fp16 [R][tau]
+Inside code word w, slot n (0..7) is coordinate j = 8w + n:
+  bits 4n .. 4n+2          table slot of the coordinate: rank if rank < 4, 5 if rank == 4
+  bit (4n + 11) mod 32     1 if x_j >= 0, 0 if x_j < 0
+"""
+import numpy as np
+
+from . import leech
+
+ALIGN = 256
+TABLE_ENTRIES = leech.NUM_CLASSES
+
+
+def _align(n: int) -> int:
+    return (n + ALIGN - 1) // ALIGN * ALIGN
+
+
+def class_table() -> np.ndarray:
+    out = np.zeros(TABLE_ENTRIES, dtype=np.uint64)
+    for c in leech.classes():
+        b = [0] * 8
+        for i, m in enumerate(c["mags"]):
+            b[i] = m
+        b[7] = c["m"] | (c["parity"] << 7)
+        out[c["id"]] = np.uint64(int.from_bytes(bytes(b), "little"))
+    return out
+
+
+def expected_planes_loop(blocks) -> dict:
+    """blocks int [n][24] (lattice points) -> cls, sign, r0, r1, r2 (each [n]);
+    one coordinate at a time, for small inputs."""
+    blocks = np.asarray(blocks, dtype=np.int64).reshape(-1, 24)
+    n = blocks.shape[0]
+    cls = np.zeros(n, dtype=np.int64)
+    sign = np.zeros(n, dtype=np.int64)
+    r = [np.zeros(n, dtype=np.int64) for _ in range(3)]
+    info = leech.classes()
+    for i in range(n):
+        x = blocks[i]
+        cid = leech.class_of(x)
+        mags = info[cid]["mags"]
+        cls[i] = cid
+        for j in range(24):
+            if x[j] < 0:
+                sign[i] |= 1 << j
+            rank = mags.index(abs(int(x[j])))
+            for p in range(3):
+                if (rank >> p) & 1:
+                    r[p][i] |= 1 << j
+    return {"cls": cls, "sign": sign, "r0": r[0], "r1": r[1], "r2": r[2]}
+
+
+def expected_planes(blocks) -> dict:
+    """Same result as expected_planes_loop, vectorized per class for large inputs."""
+    blocks = np.asarray(blocks, dtype=np.int64).reshape(-1, 24)
+    n = blocks.shape[0]
+    mag = np.abs(blocks)
+    keys = -np.sort(-mag, axis=1)
+    uniq, inv = np.unique(keys, axis=0, return_inverse=True)
+    index = leech.class_index()
+    info = leech.classes()
+    cls = np.empty(n, dtype=np.int64)
+    rank = np.empty((n, 24), dtype=np.int64)
+    inv = inv.reshape(-1)
+    for u in range(uniq.shape[0]):
+        cid = index[tuple(int(v) for v in uniq[u])]
+        sel = inv == u
+        cls[sel] = cid
+        rank[sel] = np.searchsorted(np.array(info[cid]["mags"]), mag[sel])
+    bitw = np.int64(1) << np.arange(24, dtype=np.int64)
+    out = {"cls": cls, "sign": ((blocks < 0) * bitw).sum(axis=1)}
+    for p in range(3):
+        out["r%d" % p] = (((rank >> p) & 1) * bitw).sum(axis=1)
+    return out
+
+
+def decode_planes(planes: dict) -> np.ndarray:
+    """Inverse of expected_planes: planes -> int coordinates [n][24]."""
+    info = leech.classes()
+    n = len(planes["cls"])
+    out = np.zeros((n, 24), dtype=np.int64)
+    for i in range(n):
+        mags = info[int(planes["cls"][i])]["mags"]
+        for j in range(24):
+            rank = sum(((int(planes["r%d" % p][i]) >> j) & 1) << p for p in range(3))
+            v = mags[rank]
+            out[i, j] = -v if (int(planes["sign"][i]) >> j) & 1 else v
+    return out
+
+
+def sections(rows: int, cols: int) -> dict:
+    nb, tau = cols // 24, cols % 24
+    off = {}
+    pos = 0
+    for name, size in (("table", TABLE_ENTRIES * 8), ("codes", rows * nb * 12),
+                       ("cls", rows * nb * 2), ("scale", rows * 2),
+                       ("tail", rows * tau * 2)):
+        off[name] = pos
+        pos += _align(size)
+    off["total"] = pos
+    return off
+
+
+def logical_bytes(rows: int, cols: int) -> int:
+    """LP3 weight bytes: 14 per block, 2 per row (scale), 2 per tail column."""
+    nb, tau = cols // 24, cols % 24
+    return rows * (14 * nb + 2 + 2 * tau)
+
+
+def unpack_blob(blob, rows: int, cols: int) -> dict:
+    """Parse the physical blob into logical planes, scales, tails and table."""
+    buf = np.frombuffer(bytes(blob), dtype=np.uint8)
+    off = sections(rows, cols)
+    assert buf.size == off["total"], (buf.size, off["total"])
+    nb, tau = cols // 24, cols % 24
+    table = buf[off["table"]: off["table"] + TABLE_ENTRIES * 8].view("<u8").copy()
+    words = buf[off["codes"]: off["codes"] + rows * nb * 12].view("<u4").reshape(rows * nb, 3)
+    cls = buf[off["cls"]: off["cls"] + rows * nb * 2].view("<u2").astype(np.int64)
+    scale = buf[off["scale"]: off["scale"] + rows * 2].view("<u2").copy()
+    tail = buf[off["tail"]: off["tail"] + rows * tau * 2].view("<u2").reshape(rows, tau).copy()
+    n = rows * nb
+    sign = np.zeros(n, dtype=np.int64)
+    rp = [np.zeros(n, dtype=np.int64) for _ in range(3)]
+    bad = np.zeros(n, dtype=bool)
+    for w in range(3):
+        word = words[:, w].astype(np.int64)
+        for slot in range(8):
+            j = 8 * w + slot
+            t = (word >> (4 * slot)) & 7
+            nonneg = (word >> ((4 * slot + 11) % 32)) & 1
+            rank = np.where(t < 4, t, 4)
+            bad |= (t == 4) | (t > 5)
+            sign |= (1 - nonneg) << j
+            for p in range(3):
+                rp[p] |= ((rank >> p) & 1) << j
+    return {"table": table, "cls": cls, "sign": sign, "r0": rp[0], "r1": rp[1],
+            "r2": rp[2], "scale": scale, "tail": tail, "bad_slot": bad}
