@@ -1,0 +1,182 @@
+"""Python binding of liblvq.so (argument marshalling only).
+
+Every computation runs in the library: the C++ expander on the host and the
+gfx950 kernels on the device.  This module only converts arguments (numpy
+arrays, torch tensors or raw integer pointers) into the C ABI of
+include/lvq.h and raises LvqError on a negative status.  PyTorch, when used,
+provides device memory and the current stream.  There is no fallback: if the
+library is missing, importing this package raises.
+"""
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liblvq.so")
+
+NUM_CLASSES = 302
+MAX_BATCH = 4
+
+LVQ_OK = 0
+LVQ_E_NULL = -1
+LVQ_E_SHAPE = -2
+LVQ_E_ALIGN = -3
+LVQ_E_NOT_LEECH = -4
+LVQ_E_NORM = -5
+LVQ_E_BATCH = -6
+LVQ_E_HIP = -7
+
+
+class LvqError(RuntimeError):
+    def __init__(self, code, message, index=None):
+        super().__init__("%s (status %d)%s" % (
+            message, code, "" if index is None else " at row %d, block %d" % index))
+        self.code = code
+        self.index = index
+
+
+def _load():
+    # One HIP runtime per process: PyTorch ships its own libamdhip64 (same
+    # soname).  Loading torch first makes liblvq.so bind to that runtime, so
+    # torch's device pointers and streams are valid in the library.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
+    if not os.path.exists(LIB_PATH):
+        raise ImportError("liblvq.so is not built (%s); run python -m dequant_gemv_lvq_amd.build"
+                          % LIB_PATH)
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    sig = {
+        "lvq_strerror": (ctypes.c_char_p, [i]),
+        "lvq_last_error_index": (i, [ctypes.POINTER(i), ctypes.POINTER(i)]),
+        "lvq_class_table": (i, [vp]),
+        "lvq_layout_bytes": (sz, [i, i]),
+        "lvq_expand": (i, [vp, vp, vp, i, i, vp]),
+        "lvq_gemv": (i, [vp, i, i, vp, vp, i, vp]),
+        "lvq_decode": (i, [vp, i, i, vp, vp]),
+        "bpdq_gemv": (i, [vp, vp, i, i, vp, vp, i, vp]),
+        "trellis_gemv": (i, [vp, vp, vp, i, i, vp, vp, i, vp]),
+        "fp16_gemv": (i, [vp, i, i, vp, vp, i, vp]),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(lib, name)
+        f.restype = res
+        f.argtypes = args
+    return lib
+
+
+_lib = _load()
+EXPORTED = ("lvq_strerror", "lvq_last_error_index", "lvq_class_table", "lvq_layout_bytes",
+            "lvq_expand", "lvq_gemv", "lvq_decode", "bpdq_gemv", "trellis_gemv", "fp16_gemv")
+
+
+def library():
+    return _lib
+
+
+def strerror(code: int) -> str:
+    return _lib.lvq_strerror(int(code)).decode()
+
+
+def _check(code: int, index=None):
+    if code != LVQ_OK:
+        raise LvqError(code, strerror(code), index)
+
+
+def _ptr(a):
+    """Device or host address of a torch tensor, numpy array, int or None."""
+    if a is None:
+        return None
+    if isinstance(a, int):
+        return a
+    if isinstance(a, np.ndarray):
+        if not a.flags["C_CONTIGUOUS"]:
+            raise ValueError("array must be C-contiguous")
+        return a.ctypes.data
+    if hasattr(a, "data_ptr"):
+        if not a.is_contiguous():
+            raise ValueError("tensor must be contiguous")
+        return a.data_ptr()
+    raise TypeError("unsupported argument type %r" % type(a))
+
+
+def _stream(stream):
+    if stream is None:
+        try:
+            import torch
+            return torch.cuda.current_stream().cuda_stream
+        except Exception:
+            return None
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+# ------------------------------------------------------------------ host side
+
+def class_table() -> np.ndarray:
+    out = np.zeros(NUM_CLASSES, dtype=np.uint64)
+    _check(_lib.lvq_class_table(out.ctypes.data))
+    return out
+
+
+def layout_bytes(rows: int, cols: int) -> int:
+    return int(_lib.lvq_layout_bytes(int(rows), int(cols)))
+
+
+def expand(coords, scale, tail, rows: int, cols: int) -> np.ndarray:
+    """Host expansion: coords int8 [rows][cols//24][24], scale/tail fp16 bits
+    (uint16) -> packed blob (uint8, lvq_layout_bytes long)."""
+    coords = np.ascontiguousarray(coords, dtype=np.int8)
+    scale = np.ascontiguousarray(scale, dtype=np.uint16)
+    tau = cols % 24
+    tail = None if tau == 0 else np.ascontiguousarray(tail, dtype=np.uint16)
+    n = _lib.lvq_layout_bytes(int(rows), int(cols))
+    if rows < 0 or cols < 0:
+        _check(LVQ_E_SHAPE)
+    if coords.size != rows * (cols // 24) * 24 or scale.size != rows or (
+            tail is not None and tail.size != rows * tau):
+        _check(LVQ_E_SHAPE)
+    blob = np.empty(n, dtype=np.uint8)
+    code = _lib.lvq_expand(_ptr(coords), _ptr(scale), _ptr(tail), int(rows), int(cols),
+                           blob.ctypes.data)
+    if code != LVQ_OK:
+        r, b = ctypes.c_int(), ctypes.c_int()
+        _lib.lvq_last_error_index(ctypes.byref(r), ctypes.byref(b))
+        _check(code, (r.value, b.value))
+    return blob
+
+
+def last_error_index():
+    r, b = ctypes.c_int(), ctypes.c_int()
+    _check(_lib.lvq_last_error_index(ctypes.byref(r), ctypes.byref(b)))
+    return r.value, b.value
+
+
+# ------------------------------------------------------------------ device side
+
+def gemv(blob, rows: int, cols: int, x, y, batch: int = 1, stream=None):
+    _check(_lib.lvq_gemv(_ptr(blob), int(rows), int(cols), _ptr(x), _ptr(y), int(batch),
+                         _stream(stream)))
+
+
+def decode(blob, rows: int, cols: int, out, stream=None):
+    _check(_lib.lvq_decode(_ptr(blob), int(rows), int(cols), _ptr(out), _stream(stream)))
+
+
+def bpdq_gemv(codes, coeffs, rows: int, cols: int, x, y, batch: int = 1, stream=None):
+    _check(_lib.bpdq_gemv(_ptr(codes), _ptr(coeffs), int(rows), int(cols), _ptr(x), _ptr(y),
+                          int(batch), _stream(stream)))
+
+
+def trellis_gemv(bits, table, scale, rows: int, cols: int, x, y, batch: int = 1, stream=None):
+    _check(_lib.trellis_gemv(_ptr(bits), _ptr(table), _ptr(scale), int(rows), int(cols), _ptr(x),
+                             _ptr(y), int(batch), _stream(stream)))
+
+
+def fp16_gemv(w, rows: int, cols: int, x, y, batch: int = 1, stream=None):
+    _check(_lib.fp16_gemv(_ptr(w), int(rows), int(cols), _ptr(x), _ptr(y), int(batch),
+                          _stream(stream)))

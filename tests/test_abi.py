@@ -1,0 +1,177 @@
+"""The C ABI on the CPU: exports, the host expander against the oracle, and
+argument validation of the device entry points (which return before any HIP
+call, so no GPU is needed)."""
+import os
+import re
+
+import numpy as np
+import pytest
+from hypothesis import given, settings, strategies as st
+
+import dequant_gemv_lvq_amd as lvq
+import synth
+from oracle import golay, layout, leech
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    text = open(os.path.join(ROOT, "include", "lvq.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b([a-z0-9_]+)\s*\(", text)) - {"if", "sizeof"})
+
+
+def test_library_exports_every_declared_function():
+    declared = _declared_functions()
+    assert set(declared) == set(lvq.EXPORTED)
+    for name in declared:
+        assert hasattr(lvq.library(), name), name
+
+
+def test_strerror():
+    for code in range(-7, 1):
+        assert lvq.strerror(code) and lvq.strerror(code) != "unknown status"
+    assert lvq.strerror(-99) == "unknown status"
+
+
+def test_class_table_matches_oracle():
+    assert np.array_equal(lvq.class_table(), layout.class_table())
+
+
+def test_layout_bytes_matches_oracle():
+    for r, c in [(0, 0), (1, 1), (3, 50), (4096, 12288), (4096, 4096), (12288, 4096), (7, 23)]:
+        assert lvq.layout_bytes(r, c) == layout.sections(r, c)["total"]
+    assert lvq.layout_bytes(-1, 5) == 0 and lvq.layout_bytes(5, -1) == 0
+
+
+def _check_blob(coords, scale, tail, rows, cols):
+    blob = lvq.expand(coords, scale, tail, rows, cols)
+    u = layout.unpack_blob(blob, rows, cols)
+    exp = layout.expected_planes(np.asarray(coords).reshape(-1, 24))
+    assert not u["bad_slot"].any()
+    for k in ("cls", "sign", "r0", "r1", "r2"):
+        assert np.array_equal(u[k], exp[k]), k
+    assert np.array_equal(u["table"], layout.class_table())
+    assert np.array_equal(u["scale"], scale)
+    if cols % 24:
+        assert np.array_equal(u["tail"], tail)
+    return blob, u
+
+
+def _shell2_vectors():
+    out = []
+    for i in range(24):
+        for j in range(i + 1, 24):
+            for si in (-4, 4):
+                for sj in (-4, 4):
+                    v = np.zeros(24, dtype=np.int8)
+                    v[i], v[j] = si, sj
+                    out.append(v)
+    octads = [int(w) for w in golay.codewords() if golay.weight(w) == 8]
+    for o in octads:
+        pos = [i for i in range(24) if (o >> i) & 1]
+        for s in range(256):
+            if bin(s).count("1") % 2:
+                continue
+            v = np.zeros(24, dtype=np.int8)
+            for t, p in enumerate(pos):
+                v[p] = -2 if (s >> t) & 1 else 2
+            out.append(v)
+    words = golay.codewords()
+    bits = ((words[:, None].astype(np.int64) >> np.arange(24)) & 1).astype(np.int8)
+    base = np.where(bits == 1, -1, 1).astype(np.int8)  # x = 3 mod 4 on the codeword
+    for p in range(24):
+        v = base.copy()
+        v[:, p] = np.where(bits[:, p] == 1, 3, -3)
+        out.extend(v)
+    x = np.array(out, dtype=np.int8)
+    x = x[leech.is_leech_batch(x)]
+    return x
+
+
+def test_expand_exhaustive_shell2():
+    x = _shell2_vectors()
+    assert x.shape[0] == 196560
+    rows = 196560 // 24
+    coords = x.reshape(rows, 24, 24)
+    scale = synth.fp16_bits(np.linspace(0.01, 0.03, rows))
+    blob, u = _check_blob(coords, scale, None, rows, 576)
+    assert np.array_equal(layout.decode_planes(u)[:5000], x[:5000].astype(np.int64))
+
+
+def test_expand_every_class_with_tail():
+    rng = np.random.default_rng(8)
+    blocks = [np.zeros((1, 24), dtype=np.int8)]
+    for c in leech.classes()[1:]:
+        blocks.append(synth.sample_class(c["key"], 3, rng))
+    blocks = np.concatenate(blocks)  # 904 blocks
+    rows, nb = 8, blocks.shape[0] // 8
+    cols = 24 * nb + 13
+    coords = blocks[: rows * nb].reshape(rows, nb, 24)
+    scale = synth.fp16_bits(rng.random(rows))
+    tail = synth.fp16_bits(rng.standard_normal((rows, 13)))
+    _check_blob(coords, scale, tail, rows, cols)
+
+
+@settings(max_examples=40, deadline=None)
+@given(seed=st.integers(0, 2 ** 31 - 1), rows=st.integers(1, 5), nb=st.integers(0, 9),
+       tau=st.integers(0, 23), shells=st.sampled_from([(2, 3), (2, 6), (7, 12)]))
+def test_expand_roundtrip_property(seed, rows, nb, tau, shells):
+    rng = np.random.default_rng(seed)
+    m = rng.integers(shells[0], shells[1] + 1, rows * nb)
+    coords = synth.sample_shells(m, rng).reshape(rows, nb, 24)
+    zero = rng.random((rows, nb)) < 0.1
+    coords[zero] = 0
+    scale = synth.fp16_bits(rng.standard_normal(rows))
+    tail = synth.fp16_bits(rng.standard_normal((rows, tau)))
+    _check_blob(coords, scale, tail, rows, 24 * nb + tau)
+
+
+def test_expand_errors():
+    d = synth.leech_matrix(3, 72, 3, key=(1,))
+    c = d["coords"].copy()
+    c[1, 2, 0] = -c[1, 2, 0] if c[1, 2, 0] else 2  # breaks the sum or the parity
+    if leech.is_leech(c[1, 2]):
+        c[1, 2, 5] += 2
+    with pytest.raises(lvq.LvqError) as e:
+        lvq.expand(c, d["scale"], None, 3, 72)
+    assert e.value.code == lvq.LVQ_E_NOT_LEECH and e.value.index == (1, 2)
+    far = d["coords"].copy()
+    far[2, 0] = 0
+    far[2, 0, :2] = [12, 12]  # 3 x (4, 4, 0...) is a lattice point of shell 18
+    assert leech.is_leech(far[2, 0])
+    with pytest.raises(lvq.LvqError) as e:
+        lvq.expand(far, d["scale"], None, 3, 72)
+    assert e.value.code == lvq.LVQ_E_NORM and e.value.index == (2, 0)
+    blob = lvq.expand(d["coords"], d["scale"], None, 3, 72)
+    assert blob.size == lvq.layout_bytes(3, 72)
+    assert lvq.last_error_index() == (-1, -1)
+    lib = lvq.library()
+    buf = np.zeros(lvq.layout_bytes(3, 74), dtype=np.uint8)
+    assert lib.lvq_expand(d["coords"].ctypes.data, d["scale"].ctypes.data, None, 3, 74,
+                          buf.ctypes.data) == lvq.LVQ_E_NULL  # tail required
+    assert lib.lvq_expand(None, d["scale"].ctypes.data, None, 3, 72, buf.ctypes.data) == lvq.LVQ_E_NULL
+    assert lib.lvq_expand(None, None, None, -1, 72, buf.ctypes.data) == lvq.LVQ_E_SHAPE
+    assert lib.lvq_class_table(None) == lvq.LVQ_E_NULL
+
+
+def test_device_entry_points_validate_before_launch():
+    lib = lvq.library()
+    A = 1 << 20  # a fake, 16-byte aligned address; never dereferenced
+    assert lib.lvq_gemv(A, 4, 48, A, A, 0, None) == lvq.LVQ_E_BATCH
+    assert lib.lvq_gemv(A, 4, 48, A, A, 5, None) == lvq.LVQ_E_BATCH
+    assert lib.lvq_gemv(None, 4, 48, A, A, 1, None) == lvq.LVQ_E_NULL
+    assert lib.lvq_gemv(A + 4, 4, 48, A, A, 1, None) == lvq.LVQ_E_ALIGN
+    assert lib.lvq_gemv(A, -1, 48, A, A, 1, None) == lvq.LVQ_E_SHAPE
+    assert lib.lvq_gemv(A, 4, 70000, A, A, 1, None) == lvq.LVQ_E_SHAPE
+    assert lib.lvq_gemv(A, 0, 48, A, A, 1, None) == lvq.LVQ_OK  # nothing to do
+    assert lib.lvq_decode(A, 4, 48, None, None) == lvq.LVQ_E_NULL
+    assert lib.lvq_decode(A, 4, 48, A + 8, None) == lvq.LVQ_E_ALIGN
+    assert lib.bpdq_gemv(A, A, 16, 100, A, A, 1, None) == lvq.LVQ_E_SHAPE
+    assert lib.bpdq_gemv(A, A, 16, 256, A, A, 9, None) == lvq.LVQ_E_BATCH
+    assert lib.bpdq_gemv(A, None, 16, 256, A, A, 1, None) == lvq.LVQ_E_NULL
+    assert lib.trellis_gemv(A, A, A, 16, 300, A, A, 1, None) == lvq.LVQ_E_SHAPE
+    assert lib.trellis_gemv(A, A, A, 16, 4096, A, A, 4, None) == lvq.LVQ_E_SHAPE
+    assert lib.trellis_gemv(A, A, A + 2, 16, 256, A, A, 1, None) == lvq.LVQ_E_ALIGN
+    assert lib.fp16_gemv(A, 16, 100, A, A, 1, None) == lvq.LVQ_E_SHAPE
+    assert lib.fp16_gemv(A, 16, 128, A, None, 1, None) == lvq.LVQ_E_NULL
