@@ -24,7 +24,7 @@ section starts at a multiple of 256 bytes:
   scale  fp16 [R]
   tail   fp16 [R][tau]
 Inside code word w, slot n (0..7) is coordinate j = 8w + n:
-  bits 4n .. 4n+2          table slot of the coordinate: rank if rank < 4, 5 if rank == 4
+  bits 4n .. 4n+2          table slot of the coordinate: rank + 1 (1..5)
   bit (4n + 11) mod 32     1 if x_j >= 0, 0 if x_j < 0
 """
 import numpy as np
@@ -152,8 +152,8 @@ def unpack_blob(blob, rows: int, cols: int) -> dict:
             j = 8 * w + slot
             t = (word >> (4 * slot)) & 7
             nonneg = (word >> ((4 * slot + 11) % 32)) & 1
-            rank = np.where(t < 4, t, 4)
-            bad |= (t == 4) | (t > 5)
+            rank = t - 1
+            bad |= (t == 0) | (t > 5)
             sign |= (1 - nonneg) << j
             for p in range(3):
                 rp[p] |= ((rank >> p) & 1) << j
