@@ -56,7 +56,8 @@ __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
 }
 
 // Leech decode of one coordinate pair.  `word` is a code word of a block; view
-// v (0..3) selects its slots v (low half) and v + 4 (high half).  After the
+// v (0..3) selects its slots v (low half) and v + 4 (high half), which carry
+// the adjacent coordinates 8w + 2v and 8w + 2v + 1.  After the
 // rotation by 4v, bits 0..2 and 16..18 hold the two table slots (rank + 1)
 // and bits 11 and 27 the two "non-negative" flags, so masking with 0x08070807
 // leaves the selector bytes  slot, 8*nonneg, slot, 8*nonneg.  v_perm_b32 reads

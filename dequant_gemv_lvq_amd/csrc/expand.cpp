@@ -297,7 +297,8 @@ int lvq_expand(const int8_t* coords, const uint16_t* scale, const uint16_t* tail
       uint32_t w[3] = {0, 0, 0};
       for (int j = 0; j < 24; ++j) {
         int v = x[j];
-        int n = j & 7;
+        const int jj = j & 7;
+        const int n = (jj >> 1) + 4 * (jj & 1);  // slot of coordinate j
         uint32_t slot = c.slot_of_mag[v < 0 ? -v : v];
         w[j >> 3] |= slot << (4 * n);
         if (v >= 0) w[j >> 3] |= 1u << ((4 * n + 11) & 31);

@@ -27,9 +27,13 @@
 
 namespace lvq {
 
-constexpr int kGemvThreads = 256;
-constexpr int kWavesPerWg = kGemvThreads / kWave;
-constexpr int kUnroll = 4;  // blocks per lane loaded before they are decoded
+constexpr int kMaxWgThreads = 1024;
+// blocks per lane per work item: the code words of the current and the next
+// item must stay in registers (no spills) next to B accumulator pairs
+constexpr int max_bpl(int B) { return B <= 2 ? 4 : 2; }
+// preferred item size: small items keep the decode close behind the data as it
+// arrives (about 14 MB stay in flight across the chip with two items per wave)
+constexpr int kPreferBpl = 2;
 
 struct LeechView {
   const uint64_t* table;
@@ -55,92 +59,249 @@ __device__ __forceinline__ float half_bits_to_float(uint16_t h) {
   return (float)__builtin_bit_cast(_Float16, h);
 }
 
-// LDS layout (dynamic): lut uint2[302] | xpair uint32[B][nb*12] | xtail fp16 [B][24]
-template <int B>
-__global__ void __launch_bounds__(kGemvThreads)
-leech_gemv_kernel(LeechView v, int rows, int nb, int tau, int cols, const uint16_t* __restrict__ x,
-                  float* __restrict__ y) {
-  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  uint2* lut = (uint2*)smem;
-  uint32_t* xp = (uint32_t*)(smem + LVQ_NUM_CLASSES * 8);
-  const int npair = nb * 12;
-  uint16_t* xt = (uint16_t*)(xp + B * npair);
+// Work item = (row, chunk): a chunk is up to 64 * BPL consecutive blocks of a
+// row, lane l taking blocks chunk0 + l, chunk0 + l + 64, ...  Wave w owns rows
+// w, w + W, w + 2W, ... (W waves in the grid) and walks their chunks in order;
+// its j-th item is row w + (j / nchunks) * W, chunk j % nchunks.  It issues the
+// loads of the next item before it decodes the current one, so every wave
+// keeps a whole item of code words in flight.  Rows, chunks and item counters
+// are wave-uniform (scalar registers); only the lane offset is per lane.  Loads are never predicated (a lane past the row's end re-reads the
+// row's last block and then takes the origin block instead), so the compiler
+// can wait for exactly the loads a decode step needs.
+template <int BPL>
+struct ItemRegs {
+  uint32_t w[BPL][3];
+  uint32_t c[BPL];
+  uint32_t scale, tail;  // row scale and this lane's tail value (read with the item)
+};
 
-  const int tid = threadIdx.x;
-  for (int c = tid; c < LVQ_NUM_CLASSES; c += kGemvThreads) lut[c] = leech_lut(v.table[c]);
-  // stage x: one thread per group of 8 columns (one code word), 4 pairs out
-  for (int bb = 0; bb < B; ++bb) {
-    const uint16_t* xb = x + (size_t)bb * cols;
-    for (int q = tid; q < nb * 3; q += kGemvThreads) {
-      const uint16_t* s = xb + 8 * q;
-      uint32_t p[4];
+// An item's loads come in two groups: its metadata (row scale, this lane's
+// tail value, the class ids: everything the table lookups need) and its code
+// words.  The metadata of the next items is requested before the code words
+// of the current ones, so a table lookup never waits for code words.
+template <int BPL, bool FULL>
+__device__ __forceinline__ void load_meta(const LeechView& v, int nb, int tau, int r, int chunk,
+                                          int lane, ItemRegs<BPL>& g) {
+  const int k0 = chunk * (kWave * BPL);
+  const uint16_t* clsrow = v.cls + (size_t)r * nb + k0;
+  const int lim = nb - k0;
+  // a row without tail re-reads its scale: the address is selected, not the
+  // value, so both are plain loads
+  const uint16_t* tp = tau > 0 ? v.tail + (size_t)r * tau + min(lane, tau - 1) : v.scale + r;
+  g.scale = v.scale[r];
+  g.tail = *tp;
 #pragma unroll
-      for (int k = 0; k < 4; ++k) p[k] = (uint32_t)s[k] | ((uint32_t)s[k + 4] << 16);
-      *(uint4*)(xp + bb * npair + 4 * q) = make_uint4(p[0], p[1], p[2], p[3]);
-    }
-    for (int t = tid; t < tau; t += kGemvThreads) xt[bb * 24 + t] = xb[24 * nb + t];
+  for (int u = 0; u < BPL; ++u) {
+    const int k = FULL ? lane + u * kWave : min(lane + u * kWave, lim - 1);
+    g.c[u] = clsrow[k];
   }
-  __syncthreads();
+}
 
-  const int lane = tid & (kWave - 1);
-  const int wave = blockIdx.x * kWavesPerWg + tid / kWave;
-  const int nwaves = gridDim.x * kWavesPerWg;
-  const int iters = (nb + kWave - 1) / kWave;
+template <int BPL, bool FULL>
+__device__ __forceinline__ void load_codes(const LeechView& v, int nb, int r, int chunk, int lane,
+                                           ItemRegs<BPL>& g) {
+  const int k0 = chunk * (kWave * BPL);
+  const uint32_t* crow = v.codes + ((size_t)r * nb + k0) * 3;
+  const int lim = nb - k0;
+#pragma unroll
+  for (int u = 0; u < BPL; ++u) {
+    const int k = FULL ? lane + u * kWave : min(lane + u * kWave, lim - 1);
+    g.w[u][0] = crow[3 * k + 0];
+    g.w[u][1] = crow[3 * k + 1];
+    g.w[u][2] = crow[3 * k + 2];
+  }
+}
 
-  for (int r = wave; r < rows; r += nwaves) {
-    float acc[B][2];
+// After the loads of an item have landed: blocks past the row's end become
+// origin blocks (they decode to +0).
+template <int BPL, bool FULL>
+__device__ __forceinline__ void mask_item(int nb, int chunk, int lane, ItemRegs<BPL>& g) {
+  if (FULL) return;
+  const int lim = nb - chunk * (kWave * BPL);
 #pragma unroll
-    for (int bb = 0; bb < B; ++bb) acc[bb][0] = acc[bb][1] = 0.f;
-    const uint32_t* crow = v.codes + (size_t)r * nb * 3;
-    const uint16_t* clsrow = v.cls + (size_t)r * nb;
-    for (int t0 = 0; t0 < iters; t0 += kUnroll) {
-      uint32_t w[kUnroll][3];
-      uint32_t c[kUnroll];
-      int kk[kUnroll];
+  for (int u = 0; u < BPL; ++u) {
+    const bool ok = lane + u * kWave < lim;
+    g.w[u][0] = ok ? g.w[u][0] : kZeroWord;
+    g.w[u][1] = ok ? g.w[u][1] : kZeroWord;
+    g.w[u][2] = ok ? g.w[u][2] : kZeroWord;
+    g.c[u] = ok ? g.c[u] : 0u;
+  }
+}
+
+// x staging: each thread loads kStageRegs 16-byte chunks of x into registers
+// before the code words are requested and writes them to LDS afterwards.
+constexpr int kStageRegs = 2;
+
+// LDS layout (dynamic): lut uint2[302] | x fp16 [B][kpad], kpad >= 24 * npad and
+// >= cols, a multiple of 8, with npad = nchunks * 64 * BPL blocks; columns past
+// cols are zero.  The 32-bit pair feeding view v of code word w of block k is
+// element 12k + 4w + v of a batch row.
+template <int B, int BPL, bool FULL>
+__device__ __forceinline__ void decode_item(const LeechView& v, int rows, int nb, int tau,
+                                            int nchunks, int kpad, int r, int chunk, int lane,
+                                            ItemRegs<BPL>& g, const uint2* lut,
+                                            const uint32_t* xs, float (&acc)[B][2],
+                                            float* __restrict__ y) {
+  asm volatile("" ::: "memory");  // keep this item's LDS reads inside this item
+  mask_item<BPL, FULL>(nb, chunk, lane, g);
+  const int npair = kpad / 2;
+  const uint32_t* xl = xs + (chunk * (kWave * BPL) + lane) * 12;
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        const int k = (t0 + u) * kWave + lane;
-        const bool ok = k < nb;
-        kk[u] = ok ? k : 0;
-        if (ok) {
-          w[u][0] = crow[3 * k + 0];
-          w[u][1] = crow[3 * k + 1];
-          w[u][2] = crow[3 * k + 2];
-          c[u] = min((uint32_t)clsrow[k], (uint32_t)(LVQ_NUM_CLASSES - 1));
-        } else {
-          w[u][0] = w[u][1] = w[u][2] = kZeroWord;  // origin block: decodes to +0
-          c[u] = 0u;
-        }
-      }
+  for (int u = 0; u < BPL; ++u) {
+    const uint2 l = lut[min(g.c[u], (uint32_t)(LVQ_NUM_CLASSES - 1))];
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        const uint2 l = lut[c[u]];
+    for (int wi = 0; wi < 3; ++wi) {
+      uint32_t d[4];
 #pragma unroll
-        for (int wi = 0; wi < 3; ++wi) {
-          uint32_t d[4];
+      for (int vi = 0; vi < 4; ++vi) d[vi] = leech_pair(g.w[u][wi], vi, l.x, l.y);
 #pragma unroll
-          for (int vi = 0; vi < 4; ++vi) d[vi] = leech_pair(w[u][wi], vi, l.x, l.y);
-#pragma unroll
-          for (int bb = 0; bb < B; ++bb) {
-            const uint4 xq = *(const uint4*)(xp + bb * npair + 12 * kk[u] + 4 * wi);
-            acc[bb][wi & 1] = dot2(d[0], xq.x, acc[bb][wi & 1]);
-            acc[bb][wi & 1] = dot2(d[1], xq.y, acc[bb][wi & 1]);
-            acc[bb][wi & 1] = dot2(d[2], xq.z, acc[bb][wi & 1]);
-            acc[bb][wi & 1] = dot2(d[3], xq.w, acc[bb][wi & 1]);
-          }
-        }
+      for (int bb = 0; bb < B; ++bb) {
+        const uint4 xq = *(const uint4*)(xl + bb * npair + u * (kWave * 12) + 4 * wi);
+        float& a = acc[bb][(u + wi) & 1];
+        a = dot2(d[0], xq.x, a);
+        a = dot2(d[1], xq.y, a);
+        a = dot2(d[2], xq.z, a);
+        a = dot2(d[3], xq.w, a);
       }
     }
+  }
+  if (chunk == nchunks - 1) {
     // epilogue: scale (with the 2^24 of the subnormal encoding), then the tail
-    const float s = half_bits_to_float(v.scale[r]) * 16777216.0f;
-    const uint16_t tv = lane < tau ? v.tail[(size_t)r * tau + lane] : (uint16_t)0;
+    const float s = half_bits_to_float((uint16_t)g.scale) * 16777216.0f;
+    const uint16_t tv = (uint16_t)g.tail;
+    const uint16_t* xh = (const uint16_t*)xs;
 #pragma unroll
     for (int bb = 0; bb < B; ++bb) {
       float part = (acc[bb][0] + acc[bb][1]) * s;
-      if (lane < tau) part += half_bits_to_float(tv) * half_bits_to_float(xt[bb * 24 + lane]);
+      if (lane < tau)
+        part += half_bits_to_float(tv) * half_bits_to_float(xh[bb * kpad + 24 * nb + lane]);
       const float tot = wave_sum(part);
       if (lane == 0) y[(size_t)bb * rows + r] = tot;
+      acc[bb][0] = acc[bb][1] = 0.f;
     }
+  }
+  asm volatile("" ::: "memory");
+}
+
+template <int B, int BPL, bool FULL>
+__global__ void __launch_bounds__(kMaxWgThreads)
+leech_gemv_kernel(LeechView v, int rows, int nb, int tau, int cols, int nchunks, int kpad,
+                  const uint16_t* __restrict__ x, float* __restrict__ y) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  uint2* lut = (uint2*)smem;
+  uint32_t* xs = (uint32_t*)(smem + LVQ_NUM_CLASSES * 8);
+
+  const int tid = threadIdx.x, nthr = blockDim.x;
+  const int lane = tid & (kWave - 1);
+  const int wpb = nthr / kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(blockIdx.x * wpb + (tid >> 6));
+  const int nwaves = gridDim.x * wpb;
+  // this wave's items: rows wave, wave + nwaves, ..., each with nchunks chunks
+  const int myrows = wave < rows ? (rows - 1 - wave) / nwaves + 1 : 0;
+  const int items = myrows * nchunks;
+  const int per = kpad >> 3;  // 16-byte chunks per batch row of the staged x
+  const int nq = B * per;
+  const bool vec = ((cols & 7) == 0) && ((((uintptr_t)x) & 15) == 0);
+
+  // 1. x chunks and the class-table entry (or, for an unaligned x, the whole
+  //    staging, done before any code word is requested)
+  uint4 xr[kStageRegs];
+  if (vec) {
+#pragma unroll
+    for (int i = 0; i < kStageRegs; ++i) {
+      const int q = min(tid + i * nthr, nq - 1);
+      const int bb = B == 1 ? 0 : q / per, c0 = 8 * (q - bb * per);
+      xr[i] = *(const uint4*)(x + (size_t)bb * cols + min(c0, cols - 8));
+    }
+  } else {
+    uint16_t* xh = (uint16_t*)xs;
+    for (int i = tid; i < B * kpad; i += nthr) {
+      const int bb = i / kpad, c = i - bb * kpad;
+      xh[i] = c < cols ? x[(size_t)bb * cols + c] : (uint16_t)0;
+    }
+  }
+  const uint64_t te = v.table[min(tid, LVQ_NUM_CLASSES - 1)];
+  asm volatile("" ::: "memory");
+  // 2. the first two items: metadata of both, then code words of both (a
+  //    wave with fewer items loads rows it never uses, so that the load
+  //    sequence has no branches and every later wait counts exactly)
+  ItemRegs<BPL> ia, ib;
+  int ra = wave < rows ? wave : 0, ca = 0;
+  int rb = ca + 1 == nchunks ? ra + nwaves : ra, cb = ca + 1 == nchunks ? 0 : ca + 1;
+  if (items < 2) { rb = ra; cb = ca; }
+  load_meta<BPL, FULL>(v, nb, tau, ra, ca, lane, ia);
+  load_meta<BPL, FULL>(v, nb, tau, rb, cb, lane, ib);
+  asm volatile("" ::: "memory");
+  load_codes<BPL, FULL>(v, nb, ra, ca, lane, ia);
+  load_codes<BPL, FULL>(v, nb, rb, cb, lane, ib);
+  asm volatile("" ::: "memory");
+  // 3. LDS writes (they wait only for the loads of step 1)
+  if (vec) {
+#pragma unroll
+    for (int i = 0; i < kStageRegs; ++i) {
+      const int q = tid + i * nthr;
+      const int bb = B == 1 ? 0 : q / per, c0 = 8 * (q - bb * per);
+      if (q < nq) ((uint4*)xs)[q] = c0 < cols ? xr[i] : make_uint4(0u, 0u, 0u, 0u);
+    }
+    for (int q = tid + kStageRegs * nthr; q < nq; q += nthr) {
+      const int bb = B == 1 ? 0 : q / per, c0 = 8 * (q - bb * per);
+      ((uint4*)xs)[q] = c0 < cols ? *(const uint4*)(x + (size_t)bb * cols + c0)
+                                  : make_uint4(0u, 0u, 0u, 0u);
+    }
+  }
+  for (int c = tid; c < LVQ_NUM_CLASSES; c += nthr) lut[c] = leech_lut(c == tid ? te : v.table[c]);
+  __syncthreads();
+
+  float acc[B][2];
+#pragma unroll
+  for (int bb = 0; bb < B; ++bb) acc[bb][0] = acc[bb][1] = 0.f;
+  if (items == 0) return;
+  // steady state, two items per trip with the register sets ia and ib: decode
+  // one while the other and the next one are in flight
+  auto advance = [&](int& r, int& c) {
+    // the item two places further: (r, c) -> next -> next
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      if (c + 1 == nchunks) { r += nwaves; c = 0; } else { ++c; }
+    }
+  };
+  int j = 0;
+  for (; j + 3 < items; j += 2) {
+    decode_item<B, BPL, FULL>(v, rows, nb, tau, nchunks, kpad, ra, ca, lane, ia, lut, xs, acc, y);
+    advance(ra, ca);
+    load_meta<BPL, FULL>(v, nb, tau, ra, ca, lane, ia);
+    load_codes<BPL, FULL>(v, nb, ra, ca, lane, ia);
+    decode_item<B, BPL, FULL>(v, rows, nb, tau, nchunks, kpad, rb, cb, lane, ib, lut, xs, acc, y);
+    advance(rb, cb);
+    load_meta<BPL, FULL>(v, nb, tau, rb, cb, lane, ib);
+    load_codes<BPL, FULL>(v, nb, rb, cb, lane, ib);
+  }
+  // the last one to three items
+  decode_item<B, BPL, FULL>(v, rows, nb, tau, nchunks, kpad, ra, ca, lane, ia, lut, xs, acc, y);
+  if (j + 2 < items) {
+    advance(ra, ca);
+    load_meta<BPL, FULL>(v, nb, tau, ra, ca, lane, ia);
+    load_codes<BPL, FULL>(v, nb, ra, ca, lane, ia);
+  }
+  if (j + 1 < items)
+    decode_item<B, BPL, FULL>(v, rows, nb, tau, nchunks, kpad, rb, cb, lane, ib, lut, xs, acc, y);
+  if (j + 2 < items)
+    decode_item<B, BPL, FULL>(v, rows, nb, tau, nchunks, kpad, ra, ca, lane, ia, lut, xs, acc, y);
+}
+
+// Rows shorter than one block: y = sum of the unquantized tail only.
+template <int B>
+__global__ void __launch_bounds__(256)
+leech_tail_only_kernel(LeechView v, int rows, int tau, const uint16_t* __restrict__ x,
+                       float* __restrict__ y) {
+  const int r = blockIdx.x * blockDim.x + threadIdx.x;
+  if (r >= rows) return;
+#pragma unroll
+  for (int bb = 0; bb < B; ++bb) {
+    float a = 0.f;
+    for (int t = 0; t < tau; ++t)
+      a += half_bits_to_float(v.tail[(size_t)r * tau + t]) * half_bits_to_float(x[(size_t)bb * tau + t]);
+    y[(size_t)bb * rows + r] = a;
   }
 }
 
@@ -158,8 +319,8 @@ leech_decode_kernel(LeechView v, size_t nblocks, int8_t* __restrict__ out) {
     for (int vi = 0; vi < 4; ++vi) {
       const uint32_t p = leech_pair(word, vi, l.x, l.y);
       const int lo = (int)(p & 0x3FFu), hi = (int)((p >> 16) & 0x3FFu);
-      vals[8 * wi + vi] = (int8_t)((p & 0x8000u) ? -lo : lo);
-      vals[8 * wi + vi + 4] = (int8_t)((p & 0x80000000u) ? -hi : hi);
+      vals[8 * wi + 2 * vi] = (int8_t)((p & 0x8000u) ? -lo : lo);
+      vals[8 * wi + 2 * vi + 1] = (int8_t)((p & 0x80000000u) ? -hi : hi);
     }
   }
   uint32_t* o = (uint32_t*)(out + 24 * g);
@@ -208,20 +369,54 @@ int zero_output(float* y, size_t n, hipStream_t st) {
   return launch_status();
 }
 
+template <int B, int BPL>
+int launch_leech_bpl(const LeechView& v, int rows, int cols, const uint16_t* x, float* y,
+                     hipStream_t st) {
+  const int nb = cols / 24, tau = cols % 24;
+  const int nchunks = (nb + kWave * BPL - 1) / (kWave * BPL);
+  const size_t npad = (size_t)nchunks * kWave * BPL;
+  size_t kpad = npad * 24 > (size_t)cols ? npad * 24 : (size_t)cols;
+  kpad = (kpad + 7) & ~(size_t)7;
+  const size_t lds = (size_t)LVQ_NUM_CLASSES * 8 + (size_t)B * kpad * 2;
+  if (lds > device_lds_bytes()) return LVQ_E_SHAPE;
+  const int cus = device_cus();
+  // one workgroup per CU when there are rows for at least 16 waves per CU (x
+  // is then staged once per CU); smaller workgroups otherwise, to spread rows
+  int threads = kMaxWgThreads;
+  while (threads > 256 && rows < cus * (threads / kWave)) threads /= 2;
+  const int wpb = threads / kWave;
+  long long wgs = ((long long)rows + wpb - 1) / wpb;
+  if (wgs > cus) wgs = cus;
+  if (wgs < 1) wgs = 1;
+  clear_hip_error();
+  if (nb % (kWave * BPL) == 0)
+    hipLaunchKernelGGL((leech_gemv_kernel<B, BPL, true>), dim3((unsigned)wgs), dim3(threads), lds,
+                       st, v, rows, nb, tau, cols, nchunks, (int)kpad, x, y);
+  else
+    hipLaunchKernelGGL((leech_gemv_kernel<B, BPL, false>), dim3((unsigned)wgs), dim3(threads), lds,
+                       st, v, rows, nb, tau, cols, nchunks, (int)kpad, x, y);
+  return launch_status();
+}
+
 template <int B>
 int launch_leech(const LeechView& v, int rows, int cols, const uint16_t* x, float* y,
                  hipStream_t st) {
-  const int nb = cols / 24, tau = cols % 24;
-  const size_t lds = (size_t)LVQ_NUM_CLASSES * 8 + (size_t)B * nb * 48 + (size_t)B * 24 * 2;
-  if (lds > device_lds_bytes()) return LVQ_E_SHAPE;
-  const int waves_needed = rows;
-  int wgs = (waves_needed + kWavesPerWg - 1) / kWavesPerWg;
-  const int cap = 2 * device_cus();
-  if (wgs > cap) wgs = cap;
-  clear_hip_error();
-  hipLaunchKernelGGL(leech_gemv_kernel<B>, dim3(wgs), dim3(kGemvThreads), lds, st, v, rows, nb,
-                     tau, cols, x, y);
-  return launch_status();
+  const int nb = cols / 24;
+  if (nb == 0) {
+    clear_hip_error();
+    hipLaunchKernelGGL(leech_tail_only_kernel<B>, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0,
+                       st, v, rows, cols, x, y);
+    return launch_status();
+  }
+  const int need = (nb + kWave - 1) / kWave;  // blocks per lane for one chunk per row
+  const int cap = max_bpl(B) < kPreferBpl ? max_bpl(B) : kPreferBpl;
+  const int bpl = need < 1 ? 1 : (need > cap ? cap : need);
+  if constexpr (max_bpl(B) >= 4) {
+    if (bpl == 4) return launch_leech_bpl<B, 4>(v, rows, cols, x, y, st);
+    if (bpl == 3) return launch_leech_bpl<B, 3>(v, rows, cols, x, y, st);
+  }
+  if (bpl == 2) return launch_leech_bpl<B, 2>(v, rows, cols, x, y, st);
+  return launch_leech_bpl<B, 1>(v, rows, cols, x, y, st);
 }
 
 }  // namespace lvq

@@ -23,7 +23,8 @@ section starts at a multiple of 256 bytes:
   cls    u16 [R][nb]
   scale  fp16 [R]
   tail   fp16 [R][tau]
-Inside code word w, slot n (0..7) is coordinate j = 8w + n:
+Inside code word w, slot n (0..7) is coordinate j = 8w + 2 (n % 4) + n // 4
+(slots v and v + 4 carry two adjacent columns):
   bits 4n .. 4n+2          table slot of the coordinate: rank + 1 (1..5)
   bit (4n + 11) mod 32     1 if x_j >= 0, 0 if x_j < 0
 """
@@ -149,7 +150,7 @@ def unpack_blob(blob, rows: int, cols: int) -> dict:
     for w in range(3):
         word = words[:, w].astype(np.int64)
         for slot in range(8):
-            j = 8 * w + slot
+            j = 8 * w + 2 * (slot % 4) + slot // 4
             t = (word >> (4 * slot)) & 7
             nonneg = (word >> ((4 * slot + 11) % 32)) & 1
             rank = t - 1
