@@ -40,6 +40,28 @@ size_t device_lds_bytes();
 
 // ---------------------------------------------------------------- device side
 
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_add(float v) {
+  // v + (the value DPP routes to this lane; 0 where the row is masked off)
+  const int moved = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, ROW_MASK,
+                                                0xF, false);
+  return v + __builtin_bit_cast(float, moved);
+}
+
+// Sum over the 64 lanes of a wave in a fixed order (so the result never
+// depends on timing): quad swaps, half-row and row mirrors give each row of 16
+// its sum, then two row broadcasts carry rows 0..2 into row 3.  The total is
+// valid in lane 63.
+__device__ __forceinline__ float wave_sum_lane63(float v) {
+  v = dpp_add<0xB1, 0xF>(v);   // quad_perm [1,0,3,2]
+  v = dpp_add<0x4E, 0xF>(v);   // quad_perm [2,3,0,1]
+  v = dpp_add<0x141, 0xF>(v);  // row_half_mirror
+  v = dpp_add<0x140, 0xF>(v);  // row_mirror
+  v = dpp_add<0x142, 0xA>(v);  // row_bcast:15 into rows 1 and 3
+  v = dpp_add<0x143, 0xC>(v);  // row_bcast:31 into rows 2 and 3
+  return v;
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
   // fixed butterfly: every lane ends with the same, order-independent sum
 #pragma unroll

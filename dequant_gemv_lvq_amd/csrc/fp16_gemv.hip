@@ -68,8 +68,8 @@ fp16_gemv_kernel(const uint16_t* __restrict__ W, int rows, int cols,
     }
 #pragma unroll
     for (int bb = 0; bb < B; ++bb) {
-      const float tot = wave_sum(acc[bb][0] + acc[bb][1]);
-      if (lane == 0) y[(size_t)bb * rows + r] = tot;
+      const float tot = wave_sum_lane63(acc[bb][0] + acc[bb][1]);
+      if (lane == kWave - 1) y[(size_t)bb * rows + r] = tot;
     }
   }
 }

@@ -88,12 +88,12 @@ __device__ __forceinline__ void load_meta(const LeechView& v, int nb, int tau, i
   // a row without tail re-reads its scale: the address is selected, not the
   // value, so both are plain loads
   const uint16_t* tp = tau > 0 ? v.tail + (size_t)r * tau + min(lane, tau - 1) : v.scale + r;
-  g.scale = v.scale[r];
-  g.tail = *tp;
+  g.scale = __builtin_nontemporal_load(v.scale + r);
+  g.tail = __builtin_nontemporal_load(tp);
 #pragma unroll
   for (int u = 0; u < BPL; ++u) {
     const int k = FULL ? lane + u * kWave : min(lane + u * kWave, lim - 1);
-    g.c[u] = clsrow[k];
+    g.c[u] = __builtin_nontemporal_load(clsrow + k);
   }
 }
 
@@ -106,9 +106,11 @@ __device__ __forceinline__ void load_codes(const LeechView& v, int nb, int r, in
 #pragma unroll
   for (int u = 0; u < BPL; ++u) {
     const int k = FULL ? lane + u * kWave : min(lane + u * kWave, lim - 1);
-    g.w[u][0] = crow[3 * k + 0];
-    g.w[u][1] = crow[3 * k + 1];
-    g.w[u][2] = crow[3 * k + 2];
+    // streamed once: non-temporal, so the weights do not evict x and the
+    // class table from the caches
+    g.w[u][0] = __builtin_nontemporal_load(crow + 3 * k + 0);
+    g.w[u][1] = __builtin_nontemporal_load(crow + 3 * k + 1);
+    g.w[u][2] = __builtin_nontemporal_load(crow + 3 * k + 2);
   }
 }
 
@@ -175,8 +177,8 @@ __device__ __forceinline__ void decode_item(const LeechView& v, int rows, int nb
       float part = (acc[bb][0] + acc[bb][1]) * s;
       if (lane < tau)
         part += half_bits_to_float(tv) * half_bits_to_float(xh[bb * kpad + 24 * nb + lane]);
-      const float tot = wave_sum(part);
-      if (lane == 0) y[(size_t)bb * rows + r] = tot;
+      const float tot = wave_sum_lane63(part);
+      if (lane == kWave - 1) y[(size_t)bb * rows + r] = tot;
       acc[bb][0] = acc[bb][1] = 0.f;
     }
   }

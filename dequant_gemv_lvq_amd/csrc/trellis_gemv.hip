@@ -63,8 +63,8 @@ trellis_gemv_kernel(const uint32_t* __restrict__ bits, const uint16_t* __restric
     const float s = (float)__builtin_bit_cast(_Float16, scale[r]);
 #pragma unroll
     for (int bb = 0; bb < B; ++bb) {
-      const float tot = wave_sum(acc[bb][0] + acc[bb][1]);
-      if (lane == 0) y[(size_t)bb * rows + r] = tot * s;
+      const float tot = wave_sum_lane63(acc[bb][0] + acc[bb][1]);
+      if (lane == kWave - 1) y[(size_t)bb * rows + r] = tot * s;
     }
   }
 }
