@@ -337,7 +337,7 @@ def main():
         except Exception:
             threads = 1
         passes, t_cpu = 0, 0.0
-        while t_cpu < 10.0 and passes < 20:
+        while t_cpu < 10.0 and passes < 200:
             t0 = time.perf_counter()
             w = og.leech_weights(d["coords"], d["scale"], d["tail"], COLS)
             y64, bound = og.gemv(w, x)
