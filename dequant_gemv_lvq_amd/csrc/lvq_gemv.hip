@@ -10,16 +10,20 @@
 // gfx950 design.  One wave64 owns one row at a time (rows are grid-strided
 // over all waves).  Lane l takes blocks l, l + 64, ... of the row, so every
 // load instruction of a wave reads one contiguous run of the row's code words
-// (12 bytes per lane) and class ids (2 bytes per lane).  x is staged in LDS
-// once per workgroup in "pair order": for block b, code word w and view v the
-// 32-bit pair (x[24b + 8w + v], x[24b + 8w + v + 4]), so one ds_read_b128
-// feeds the four views of a code word.  The class table is staged in LDS as
-// 8-byte byte-LUTs.  Per coordinate pair the decode is
+// (12 bytes per lane) and class ids (2 bytes per lane).  The loads are raw
+// buffer loads: the per-lane offset is fixed, the item's position is in the
+// scalar buffer resource, and a load past the row's end reads 0 (which
+// decodes to +0), so no vector instruction goes to addressing or masking.
+// x is copied into LDS once per workgroup by buffer loads that write LDS
+// directly (no registers, no vector instructions); the pair feeding view v of
+// code word w of block k is the natural fp16 pair at column 24k + 8w + 2v.
+// The class table is staged in LDS as 8-byte byte-LUTs.  Per coordinate pair
+// the decode is
 //     rotate (v_alignbit), mask (v_and), byte LUT (v_perm)
 // giving two signed magnitudes as exact fp16 subnormals (value * 2^-24), and
 // one v_dot2_f32_f16 multiplies them with the x pair into an fp32
 // accumulator; the 2^24 is folded into the row scale.  No MFMA: at batch 1
-// this is a stream over HBM.  The wave reduction is a fixed butterfly, so the
+// this is a stream over HBM.  The wave reduction is a fixed DPP tree, so the
 // result does not depend on timing.
 
 #include "common.h"
@@ -31,9 +35,23 @@ constexpr int kMaxWgThreads = 1024;
 // blocks per lane per work item: the code words of the current and the next
 // item must stay in registers (no spills) next to B accumulator pairs
 constexpr int max_bpl(int B) { return B <= 2 ? 4 : 2; }
-// preferred item size: small items keep the decode close behind the data as it
-// arrives (about 14 MB stay in flight across the chip with two items per wave)
-constexpr int kPreferBpl = 2;
+
+// Blocks per lane for rows of nb blocks: the fewest idle lane slots in the
+// row's last chunk; among equals 2 (small items keep the decode close behind
+// the data as it arrives), then 3, 1, 4.
+inline int choose_bpl(int nb, int maxb) {
+  static const int order[4] = {2, 3, 1, 4};
+  int best = 1;
+  long long best_idle = -1;
+  for (int i = 0; i < 4; ++i) {
+    const int b = order[i];
+    if (b > maxb) continue;
+    const long long per = (long long)kWave * b;
+    const long long idle = (nb + per - 1) / per * per - nb;
+    if (best_idle < 0 || idle < best_idle) { best = b; best_idle = idle; }
+  }
+  return best;
+}
 
 struct LeechView {
   const uint64_t* table;
@@ -59,93 +77,88 @@ __device__ __forceinline__ float half_bits_to_float(uint16_t h) {
   return (float)__builtin_bit_cast(_Float16, h);
 }
 
+// Raw buffer resources (gfx9 family: untyped, 32-bit data format).  A load
+// at a byte offset at or past `bytes` returns 0 without touching memory,
+// which is how the loads of a chunk that runs past its row's end stay in
+// bounds: every code word and class id past the end reads as 0, and the
+// all-zero code word in class 0 decodes to +0 (byte 0 of class 0's LUT is
+// 0x00, see stage_lut).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+// cache policy of the streamed loads: non-temporal (read once; they should
+// not evict x, the class table or the row scales)
+constexpr int kStream = 2;
+
 // Work item = (row, chunk): a chunk is up to 64 * BPL consecutive blocks of a
 // row, lane l taking blocks chunk0 + l, chunk0 + l + 64, ...  Wave w owns rows
 // w, w + W, w + 2W, ... (W waves in the grid) and walks their chunks in order;
 // its j-th item is row w + (j / nchunks) * W, chunk j % nchunks.  It issues the
-// loads of the next item before it decodes the current one, so every wave
-// keeps a whole item of code words in flight.  Rows, chunks and item counters
-// are wave-uniform (scalar registers); only the lane offset is per lane.  Loads are never predicated (a lane past the row's end re-reads the
-// row's last block and then takes the origin block instead), so the compiler
-// can wait for exactly the loads a decode step needs.
+// loads of the next items before it decodes the current one, so every wave
+// keeps two items of code words in flight.  Rows, chunks and item counters
+// are wave-uniform (scalar registers): each item's addresses are scalar buffer
+// resources plus a fixed per-lane offset, so no vector instruction is spent on
+// addressing.
 template <int BPL>
 struct ItemRegs {
   uint32_t w[BPL][3];
   uint32_t c[BPL];
-  uint32_t scale, tail;  // row scale and this lane's tail value (read with the item)
+  uint32_t tail;   // this lane's tail value (0 for lanes >= tau)
+  uint32_t scale;  // the row's fp16 scale
 };
 
-// An item's loads come in two groups: its metadata (row scale, this lane's
-// tail value, the class ids: everything the table lookups need) and its code
-// words.  The metadata of the next items is requested before the code words
-// of the current ones, so a table lookup never waits for code words.
-template <int BPL, bool FULL>
+// An item's loads come in two groups: its metadata (class ids, this lane's
+// tail value, the row scale: everything the table lookups and the epilogue
+// need) and its code words.
+template <int BPL>
 __device__ __forceinline__ void load_meta(const LeechView& v, int nb, int tau, int r, int chunk,
                                           int lane, ItemRegs<BPL>& g) {
   const int k0 = chunk * (kWave * BPL);
-  const uint16_t* clsrow = v.cls + (size_t)r * nb + k0;
-  const int lim = nb - k0;
-  // a row without tail re-reads its scale: the address is selected, not the
-  // value, so both are plain loads
-  const uint16_t* tp = tau > 0 ? v.tail + (size_t)r * tau + min(lane, tau - 1) : v.scale + r;
-  g.scale = __builtin_nontemporal_load(v.scale + r);
-  g.tail = __builtin_nontemporal_load(tp);
+  const auto rc = buffer_rsrc(v.cls + (size_t)r * nb + k0, (uint32_t)(nb - k0) * 2);
 #pragma unroll
-  for (int u = 0; u < BPL; ++u) {
-    const int k = FULL ? lane + u * kWave : min(lane + u * kWave, lim - 1);
-    g.c[u] = __builtin_nontemporal_load(clsrow + k);
-  }
+  for (int u = 0; u < BPL; ++u)
+    g.c[u] = __builtin_amdgcn_raw_buffer_load_b16(rc, (lane + u * kWave) * 2, 0, kStream);
+  const auto rt = buffer_rsrc(v.tail + (size_t)r * tau, (uint32_t)tau * 2);
+  g.tail = __builtin_amdgcn_raw_buffer_load_b16(rt, lane * 2, 0, 0);
+  // the row scale, read by every lane (one transaction); a vector load, so
+  // that waiting for it never holds up the LDS reads
+  const auto rs = buffer_rsrc(v.scale + r, 2);
+  g.scale = __builtin_amdgcn_raw_buffer_load_b16(rs, 0, 0, 0);
 }
 
-template <int BPL, bool FULL>
+template <int BPL>
 __device__ __forceinline__ void load_codes(const LeechView& v, int nb, int r, int chunk, int lane,
                                            ItemRegs<BPL>& g) {
   const int k0 = chunk * (kWave * BPL);
-  const uint32_t* crow = v.codes + ((size_t)r * nb + k0) * 3;
-  const int lim = nb - k0;
+  const auto rw = buffer_rsrc(v.codes + ((size_t)r * nb + k0) * 3, (uint32_t)(nb - k0) * 12);
 #pragma unroll
   for (int u = 0; u < BPL; ++u) {
-    const int k = FULL ? lane + u * kWave : min(lane + u * kWave, lim - 1);
-    // streamed once: non-temporal, so the weights do not evict x and the
-    // class table from the caches
-    g.w[u][0] = __builtin_nontemporal_load(crow + 3 * k + 0);
-    g.w[u][1] = __builtin_nontemporal_load(crow + 3 * k + 1);
-    g.w[u][2] = __builtin_nontemporal_load(crow + 3 * k + 2);
+    const int o = (lane + u * kWave) * 12;
+    g.w[u][0] = __builtin_amdgcn_raw_buffer_load_b32(rw, o, 0, kStream);
+    g.w[u][1] = __builtin_amdgcn_raw_buffer_load_b32(rw, o + 4, 0, kStream);
+    g.w[u][2] = __builtin_amdgcn_raw_buffer_load_b32(rw, o + 8, 0, kStream);
   }
 }
 
-// After the loads of an item have landed: blocks past the row's end become
-// origin blocks (they decode to +0).
-template <int BPL, bool FULL>
-__device__ __forceinline__ void mask_item(int nb, int chunk, int lane, ItemRegs<BPL>& g) {
-  if (FULL) return;
-  const int lim = nb - chunk * (kWave * BPL);
-#pragma unroll
-  for (int u = 0; u < BPL; ++u) {
-    const bool ok = lane + u * kWave < lim;
-    g.w[u][0] = ok ? g.w[u][0] : kZeroWord;
-    g.w[u][1] = ok ? g.w[u][1] : kZeroWord;
-    g.w[u][2] = ok ? g.w[u][2] : kZeroWord;
-    g.c[u] = ok ? g.c[u] : 0u;
-  }
+// Both groups, metadata first, so a table lookup never waits for code words.
+template <int BPL>
+__device__ __forceinline__ void load_item(const LeechView& v, int nb, int tau, int r, int chunk,
+                                          int lane, ItemRegs<BPL>& g) {
+  load_meta<BPL>(v, nb, tau, r, chunk, lane, g);
+  load_codes<BPL>(v, nb, r, chunk, lane, g);
 }
-
-// x staging: each thread loads kStageRegs 16-byte chunks of x into registers
-// before the code words are requested and writes them to LDS afterwards.
-constexpr int kStageRegs = 2;
 
 // LDS layout (dynamic): lut uint2[302] | x fp16 [B][kpad], kpad >= 24 * npad and
-// >= cols, a multiple of 8, with npad = nchunks * 64 * BPL blocks; columns past
+// >= cols, a multiple of 512, with npad = nchunks * 64 * BPL blocks; columns past
 // cols are zero.  The 32-bit pair feeding view v of code word w of block k is
-// element 12k + 4w + v of a batch row.
-template <int B, int BPL, bool FULL>
-__device__ __forceinline__ void decode_item(const LeechView& v, int rows, int nb, int tau,
-                                            int nchunks, int kpad, int r, int chunk, int lane,
-                                            ItemRegs<BPL>& g, const uint2* lut,
-                                            const uint32_t* xs, float (&acc)[B][2],
-                                            float* __restrict__ y) {
+// element 12k + 4w + v of a batch row (natural column order).
+template <int B, int BPL>
+__device__ __forceinline__ void decode_item(int rows, int nb, int tau, int nchunks, int kpad,
+                                            int r, int chunk, int lane, const ItemRegs<BPL>& g,
+                                            const uint2* lut, const uint32_t* xs,
+                                            float (&acc)[B][2], float* __restrict__ y) {
   asm volatile("" ::: "memory");  // keep this item's LDS reads inside this item
-  mask_item<BPL, FULL>(nb, chunk, lane, g);
   const int npair = kpad / 2;
   const uint32_t* xl = xs + (chunk * (kWave * BPL) + lane) * 12;
 #pragma unroll
@@ -170,13 +183,13 @@ __device__ __forceinline__ void decode_item(const LeechView& v, int rows, int nb
   if (chunk == nchunks - 1) {
     // epilogue: scale (with the 2^24 of the subnormal encoding), then the tail
     const float s = half_bits_to_float((uint16_t)g.scale) * 16777216.0f;
-    const uint16_t tv = (uint16_t)g.tail;
     const uint16_t* xh = (const uint16_t*)xs;
 #pragma unroll
     for (int bb = 0; bb < B; ++bb) {
       float part = (acc[bb][0] + acc[bb][1]) * s;
       if (lane < tau)
-        part += half_bits_to_float(tv) * half_bits_to_float(xh[bb * kpad + 24 * nb + lane]);
+        part += half_bits_to_float((uint16_t)g.tail) *
+                half_bits_to_float(xh[bb * kpad + 24 * nb + lane]);
       const float tot = wave_sum_lane63(part);
       if (lane == kWave - 1) y[(size_t)bb * rows + r] = tot;
       acc[bb][0] = acc[bb][1] = 0.f;
@@ -185,7 +198,16 @@ __device__ __forceinline__ void decode_item(const LeechView& v, int rows, int nb
   asm volatile("" ::: "memory");
 }
 
-template <int B, int BPL, bool FULL>
+// The class table staged as per-class byte LUTs (leech_lut); class 0 gets
+// 0x00 in byte 0 so that an all-zero code word reads as +0 (valid class-0
+// code words never select byte 0).
+__device__ __forceinline__ uint2 stage_lut(int c, uint64_t entry) {
+  uint2 l = leech_lut(entry);
+  if (c == 0) l.x &= ~0xFFu;
+  return l;
+}
+
+template <int B, int BPL>
 __global__ void __launch_bounds__(kMaxWgThreads)
 leech_gemv_kernel(LeechView v, int rows, int nb, int tau, int cols, int nchunks, int kpad,
                   const uint16_t* __restrict__ x, float* __restrict__ y) {
@@ -205,15 +227,20 @@ leech_gemv_kernel(LeechView v, int rows, int nb, int tau, int cols, int nchunks,
   const int nq = B * per;
   const bool vec = ((cols & 7) == 0) && ((((uintptr_t)x) & 15) == 0);
 
-  // 1. x chunks and the class-table entry (or, for an unaligned x, the whole
-  //    staging, done before any code word is requested)
-  uint4 xr[kStageRegs];
+  // 1. x into LDS.  With whole 16-byte units per batch row: buffer loads
+  //    that write LDS directly, 1 KiB per wave instruction, columns past
+  //    cols reading as 0 (kpad is a multiple of 512 columns, so a 1 KiB unit
+  //    never straddles two batch rows).  Otherwise element by element.
   if (vec) {
-#pragma unroll
-    for (int i = 0; i < kStageRegs; ++i) {
-      const int q = min(tid + i * nthr, nq - 1);
-      const int bb = B == 1 ? 0 : q / per, c0 = 8 * (q - bb * per);
-      xr[i] = *(const uint4*)(x + (size_t)bb * cols + min(c0, cols - 8));
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    for (int q = wv; q * kWave < nq; q += wpb) {
+      const int u0 = q * kWave;  // first 16-byte unit of this KiB
+      const int bb = B == 1 ? 0 : u0 / per;
+      const int c0 = 8 * (u0 - bb * per);
+      const auto rx = buffer_rsrc(x + (size_t)bb * cols, (uint32_t)cols * 2);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rx, (__attribute__((address_space(3))) void*)((uint8_t*)xs + (size_t)u0 * 16), 16,
+          lane * 16, c0 * 2, 0, 0);
     }
   } else {
     uint16_t* xh = (uint16_t*)xs;
@@ -224,34 +251,18 @@ leech_gemv_kernel(LeechView v, int rows, int nb, int tau, int cols, int nchunks,
   }
   const uint64_t te = v.table[min(tid, LVQ_NUM_CLASSES - 1)];
   asm volatile("" ::: "memory");
-  // 2. the first two items: metadata of both, then code words of both (a
-  //    wave with fewer items loads rows it never uses, so that the load
-  //    sequence has no branches and every later wait counts exactly)
+  // 2. the first two items (a wave with fewer items loads rows it never
+  //    uses, so that the load sequence has no branches and every later wait
+  //    counts exactly)
   ItemRegs<BPL> ia, ib;
   int ra = wave < rows ? wave : 0, ca = 0;
   int rb = ca + 1 == nchunks ? ra + nwaves : ra, cb = ca + 1 == nchunks ? 0 : ca + 1;
   if (items < 2) { rb = ra; cb = ca; }
-  load_meta<BPL, FULL>(v, nb, tau, ra, ca, lane, ia);
-  load_meta<BPL, FULL>(v, nb, tau, rb, cb, lane, ib);
+  load_item<BPL>(v, nb, tau, ra, ca, lane, ia);
+  load_item<BPL>(v, nb, tau, rb, cb, lane, ib);
   asm volatile("" ::: "memory");
-  load_codes<BPL, FULL>(v, nb, ra, ca, lane, ia);
-  load_codes<BPL, FULL>(v, nb, rb, cb, lane, ib);
-  asm volatile("" ::: "memory");
-  // 3. LDS writes (they wait only for the loads of step 1)
-  if (vec) {
-#pragma unroll
-    for (int i = 0; i < kStageRegs; ++i) {
-      const int q = tid + i * nthr;
-      const int bb = B == 1 ? 0 : q / per, c0 = 8 * (q - bb * per);
-      if (q < nq) ((uint4*)xs)[q] = c0 < cols ? xr[i] : make_uint4(0u, 0u, 0u, 0u);
-    }
-    for (int q = tid + kStageRegs * nthr; q < nq; q += nthr) {
-      const int bb = B == 1 ? 0 : q / per, c0 = 8 * (q - bb * per);
-      ((uint4*)xs)[q] = c0 < cols ? *(const uint4*)(x + (size_t)bb * cols + c0)
-                                  : make_uint4(0u, 0u, 0u, 0u);
-    }
-  }
-  for (int c = tid; c < LVQ_NUM_CLASSES; c += nthr) lut[c] = leech_lut(c == tid ? te : v.table[c]);
+  // 3. the class table into LDS; the barrier also waits for x
+  for (int c = tid; c < LVQ_NUM_CLASSES; c += nthr) lut[c] = stage_lut(c, c == tid ? te : v.table[c]);
   __syncthreads();
 
   float acc[B][2];
@@ -269,26 +280,23 @@ leech_gemv_kernel(LeechView v, int rows, int nb, int tau, int cols, int nchunks,
   };
   int j = 0;
   for (; j + 3 < items; j += 2) {
-    decode_item<B, BPL, FULL>(v, rows, nb, tau, nchunks, kpad, ra, ca, lane, ia, lut, xs, acc, y);
+    decode_item<B, BPL>(rows, nb, tau, nchunks, kpad, ra, ca, lane, ia, lut, xs, acc, y);
     advance(ra, ca);
-    load_meta<BPL, FULL>(v, nb, tau, ra, ca, lane, ia);
-    load_codes<BPL, FULL>(v, nb, ra, ca, lane, ia);
-    decode_item<B, BPL, FULL>(v, rows, nb, tau, nchunks, kpad, rb, cb, lane, ib, lut, xs, acc, y);
+    load_item<BPL>(v, nb, tau, ra, ca, lane, ia);
+    decode_item<B, BPL>(rows, nb, tau, nchunks, kpad, rb, cb, lane, ib, lut, xs, acc, y);
     advance(rb, cb);
-    load_meta<BPL, FULL>(v, nb, tau, rb, cb, lane, ib);
-    load_codes<BPL, FULL>(v, nb, rb, cb, lane, ib);
+    load_item<BPL>(v, nb, tau, rb, cb, lane, ib);
   }
   // the last one to three items
-  decode_item<B, BPL, FULL>(v, rows, nb, tau, nchunks, kpad, ra, ca, lane, ia, lut, xs, acc, y);
+  decode_item<B, BPL>(rows, nb, tau, nchunks, kpad, ra, ca, lane, ia, lut, xs, acc, y);
   if (j + 2 < items) {
     advance(ra, ca);
-    load_meta<BPL, FULL>(v, nb, tau, ra, ca, lane, ia);
-    load_codes<BPL, FULL>(v, nb, ra, ca, lane, ia);
+    load_item<BPL>(v, nb, tau, ra, ca, lane, ia);
   }
   if (j + 1 < items)
-    decode_item<B, BPL, FULL>(v, rows, nb, tau, nchunks, kpad, rb, cb, lane, ib, lut, xs, acc, y);
+    decode_item<B, BPL>(rows, nb, tau, nchunks, kpad, rb, cb, lane, ib, lut, xs, acc, y);
   if (j + 2 < items)
-    decode_item<B, BPL, FULL>(v, rows, nb, tau, nchunks, kpad, ra, ca, lane, ia, lut, xs, acc, y);
+    decode_item<B, BPL>(rows, nb, tau, nchunks, kpad, ra, ca, lane, ia, lut, xs, acc, y);
 }
 
 // Rows shorter than one block: y = sum of the unquantized tail only.
@@ -378,7 +386,7 @@ int launch_leech_bpl(const LeechView& v, int rows, int cols, const uint16_t* x, 
   const int nchunks = (nb + kWave * BPL - 1) / (kWave * BPL);
   const size_t npad = (size_t)nchunks * kWave * BPL;
   size_t kpad = npad * 24 > (size_t)cols ? npad * 24 : (size_t)cols;
-  kpad = (kpad + 7) & ~(size_t)7;
+  kpad = (kpad + 511) & ~(size_t)511;
   const size_t lds = (size_t)LVQ_NUM_CLASSES * 8 + (size_t)B * kpad * 2;
   if (lds > device_lds_bytes()) return LVQ_E_SHAPE;
   const int cus = device_cus();
@@ -391,12 +399,8 @@ int launch_leech_bpl(const LeechView& v, int rows, int cols, const uint16_t* x, 
   if (wgs > cus) wgs = cus;
   if (wgs < 1) wgs = 1;
   clear_hip_error();
-  if (nb % (kWave * BPL) == 0)
-    hipLaunchKernelGGL((leech_gemv_kernel<B, BPL, true>), dim3((unsigned)wgs), dim3(threads), lds,
-                       st, v, rows, nb, tau, cols, nchunks, (int)kpad, x, y);
-  else
-    hipLaunchKernelGGL((leech_gemv_kernel<B, BPL, false>), dim3((unsigned)wgs), dim3(threads), lds,
-                       st, v, rows, nb, tau, cols, nchunks, (int)kpad, x, y);
+  hipLaunchKernelGGL((leech_gemv_kernel<B, BPL>), dim3((unsigned)wgs), dim3(threads), lds, st, v,
+                     rows, nb, tau, cols, nchunks, (int)kpad, x, y);
   return launch_status();
 }
 
@@ -410,11 +414,11 @@ int launch_leech(const LeechView& v, int rows, int cols, const uint16_t* x, floa
                        st, v, rows, cols, x, y);
     return launch_status();
   }
-  const int need = (nb + kWave - 1) / kWave;  // blocks per lane for one chunk per row
-  const int cap = max_bpl(B) < kPreferBpl ? max_bpl(B) : kPreferBpl;
-  const int bpl = need < 1 ? 1 : (need > cap ? cap : need);
+  const int bpl = choose_bpl(nb, max_bpl(B));
   if constexpr (max_bpl(B) >= 4) {
     if (bpl == 4) return launch_leech_bpl<B, 4>(v, rows, cols, x, y, st);
+  }
+  if constexpr (max_bpl(B) >= 3) {
     if (bpl == 3) return launch_leech_bpl<B, 3>(v, rows, cols, x, y, st);
   }
   if (bpl == 2) return launch_leech_bpl<B, 2>(v, rows, cols, x, y, st);
