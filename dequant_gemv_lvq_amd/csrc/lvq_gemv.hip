@@ -36,19 +36,44 @@ constexpr int kMaxWgThreads = 1024;
 // item must stay in registers (no spills) next to B accumulator pairs
 constexpr int max_bpl(int B) { return B <= 2 ? 4 : 2; }
 
-// Blocks per lane for rows of nb blocks: the fewest idle lane slots in the
-// row's last chunk; among equals 2 (small items keep the decode close behind
-// the data as it arrives), then 3, 1, 4.
-inline int choose_bpl(int nb, int maxb) {
-  static const int order[4] = {2, 3, 1, 4};
-  int best = 1;
+// Workgroup size for `rows` rows: 1024 threads (x staged once per 16 waves)
+// when there are rows for 16 waves on every CU, smaller otherwise so the rows
+// spread over all CUs.
+inline int wg_threads(int rows, int cus) {
+  int threads = kMaxWgThreads;
+  while (threads > 256 && rows < cus * (threads / kWave)) threads /= 2;
+  return threads;
+}
+
+// Blocks per lane for rows of nb blocks.  First the fewest idle lane slots in
+// a row's last chunk; among those the largest (fewest items, least per-item
+// work) unless there are three to five waves per SIMD, where the one giving
+// each wave closest to four items wins (enough loads in flight behind the
+// decode).  Measured on MI355X over the shapes of a Qwen3-8B layer.
+inline int choose_bpl(int nb, int maxb, int rows, int cus) {
+  const int wpb = wg_threads(rows, cus) / kWave;
+  long long waves = ((long long)rows + wpb - 1) / wpb;
+  if (waves > 2LL * cus) waves = 2LL * cus;  // up to two workgroups per CU
+  waves *= wpb;
+  const long long rows_per_wave = ((long long)rows + waves - 1) / waves;
+  // with two or fewer waves per SIMD an item's loads cannot hide behind
+  // another wave's decode anyway, and with six or more they always can: in
+  // both cases fewer, larger items win
+  const bool largest = waves >= 6LL * 4 * cus || waves <= 2LL * 4 * cus;
   long long best_idle = -1;
-  for (int i = 0; i < 4; ++i) {
-    const int b = order[i];
-    if (b > maxb) continue;
+  for (int b = 1; b <= maxb; ++b) {
     const long long per = (long long)kWave * b;
     const long long idle = (nb + per - 1) / per * per - nb;
-    if (best_idle < 0 || idle < best_idle) { best = b; best_idle = idle; }
+    if (best_idle < 0 || idle < best_idle) best_idle = idle;
+  }
+  int best = 1;
+  long long best_score = -1;
+  for (int b = 1; b <= maxb; ++b) {
+    const long long per = (long long)kWave * b;
+    if ((nb + per - 1) / per * per - nb != best_idle) continue;
+    const long long items = rows_per_wave * ((nb + per - 1) / per);
+    const long long score = largest ? b : -(items > 4 ? items - 4 : 4 - items) * 8 + b;
+    if (best_score == -1 || score > best_score) { best = b; best_score = score; }
   }
   return best;
 }
@@ -163,7 +188,7 @@ __device__ __forceinline__ void decode_item(int rows, int nb, int tau, int nchun
   const uint32_t* xl = xs + (chunk * (kWave * BPL) + lane) * 12;
 #pragma unroll
   for (int u = 0; u < BPL; ++u) {
-    const uint2 l = lut[min(g.c[u], (uint32_t)(LVQ_NUM_CLASSES - 1))];
+    const uint2 l = lut[g.c[u]];  // ids < 302 by construction (lvq_expand)
 #pragma unroll
     for (int wi = 0; wi < 3; ++wi) {
       uint32_t d[4];
@@ -390,13 +415,21 @@ int launch_leech_bpl(const LeechView& v, int rows, int cols, const uint16_t* x, 
   const size_t lds = (size_t)LVQ_NUM_CLASSES * 8 + (size_t)B * kpad * 2;
   if (lds > device_lds_bytes()) return LVQ_E_SHAPE;
   const int cus = device_cus();
-  // one workgroup per CU when there are rows for at least 16 waves per CU (x
-  // is then staged once per CU); smaller workgroups otherwise, to spread rows
-  int threads = kMaxWgThreads;
-  while (threads > 256 && rows < cus * (threads / kWave)) threads /= 2;
+  const int threads = wg_threads(rows, cus);
   const int wpb = threads / kWave;
+  // as many workgroups as fit on the chip at once (one or two per CU, by
+  // registers and LDS), rows grid-strided over their waves
+  static int occupancy[3][2] = {{0, 0}, {0, 0}, {0, 0}};
+  const int ti = threads == 1024 ? 0 : threads == 512 ? 1 : 2, li = lds > 64 * 1024;
+  if (!occupancy[ti][li]) {
+    int n = 1;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, leech_gemv_kernel<B, BPL>, threads, lds) !=
+            hipSuccess || n < 1)
+      n = 1;
+    occupancy[ti][li] = n > 2 ? 2 : n;
+  }
   long long wgs = ((long long)rows + wpb - 1) / wpb;
-  if (wgs > cus) wgs = cus;
+  if (wgs > (long long)occupancy[ti][li] * cus) wgs = (long long)occupancy[ti][li] * cus;
   if (wgs < 1) wgs = 1;
   clear_hip_error();
   hipLaunchKernelGGL((leech_gemv_kernel<B, BPL>), dim3((unsigned)wgs), dim3(threads), lds, st, v,
@@ -414,7 +447,7 @@ int launch_leech(const LeechView& v, int rows, int cols, const uint16_t* x, floa
                        st, v, rows, cols, x, y);
     return launch_status();
   }
-  const int bpl = choose_bpl(nb, max_bpl(B));
+  const int bpl = choose_bpl(nb, max_bpl(B), rows, device_cus());
   if constexpr (max_bpl(B) >= 4) {
     if (bpl == 4) return launch_leech_bpl<B, 4>(v, rows, cols, x, y, st);
   }
