@@ -1,21 +1,30 @@
 #!/usr/bin/env python3
 """Benchmark of the Leech-lattice dequantize-plus-matvec hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--trials T]
+                    [--no-arms] [--no-stack] [--no-cpu] [--profile KERNEL]
 
 A step is one batch-1 Leech GEMV y = W x at 4096 x 12288 (down_proj-shaped,
-shells 2..6 with P(m) ~ 2^-m, the workload the metric is quoted on), on seeded
-synthetic inputs already resident in HBM.  Parity of every kernel at exactly
-these shapes and seeds is the GPU test suite's job; here the cpu_baseline leg,
-which runs the f64 oracle on the same workload to time it, also reports the
-largest error ratio of the timed Leech output.  To keep the 256 MB Infinity
-Cache from serving the weights,
-the timed launches rotate over enough copies of the blob to touch more than
-512 MB.  Per-launch HIP events on the launch stream give the kernel's average
-duration (roofline.achieved); the region's events give whole-job throughput
-(value).  The comparison arms (fp16 control, BPDQ, bitshift trellis) are timed
-the same way and reported under "arms".  The oracle is timed on the host cores
-as cpu_baseline.  Prints one JSON line.
+shells 2..6 with P(m) ~ 2^-m), the workload the metric is quoted on, on
+seeded synthetic inputs already resident in HBM.  W warm-up launches, then T
+trials of K back-to-back launches on one stream, each trial bracketed by HIP
+events on that stream; the median trial gives `value` (weight-stream GB/s on
+the layout's algorithmic bytes) and `roofline.achieved`.  Every timed
+workload rotates over enough copies of its weights to touch more than 512 MB,
+so the 256 MB Infinity Cache never serves them.
+
+Beside the headline the JSON line carries one record per arm x config x
+batch (Leech at every config shape and batch 1 and 4, the BPDQ and bitshift-
+trellis arms, the fp16 dense control at the same shapes), each with its
+fraction of a read-only streaming kernel over the same bytes and rotation
+(lvq_stream_read), the metric shape captured in a HIP graph, the Qwen3-8B
+Leech stack of 252 GEMVs (GEMV-only time on precomputed inputs, and the
+dependent chain with its renormalisations), and the f64 oracle timed on the
+host cores (cpu_baseline: all cores; the per-record oracle times: one core
+and all cores, reconstruction and matvec separately).  Parity of every
+kernel at these shapes is the GPU test suite's job; the cpu_baseline leg,
+which runs the oracle on the timed workload anyway, also reports the largest
+error ratio of the timed Leech output.
 
 --profile KERNEL runs only that kernel's launch loop (for rocprofv3 counters);
 --profile copy runs a plain fp32->fp16 conversion of known size, the
@@ -33,10 +42,10 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E datasheet peak
-MALL_BYTES = 256 << 20          # Infinity Cache
-ROTATE_BYTES = 512 << 20        # bytes touched per rotation of copies
+ROTATE_BYTES = 512 << 20        # bytes touched per rotation of copies (> 256 MB MALL)
 METRIC = "µs/GEMV and weight-stream GB/s as % of HBM peak, batch 1, 4096×12288"
 ROWS, COLS = 4096, 12288
+QWEN_LAYERS = 36
 
 
 def parse():
@@ -44,9 +53,11 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=400)
     p.add_argument("--warmup", type=int, default=40)
-    p.add_argument("--copies", type=int, default=0, help="blob copies (0: enough for 512 MB)")
+    p.add_argument("--trials", type=int, default=7)
     p.add_argument("--no-arms", action="store_true")
+    p.add_argument("--no-stack", action="store_true")
     p.add_argument("--no-cpu", action="store_true")
+    p.add_argument("--stack-layers", type=int, default=QWEN_LAYERS)
     p.add_argument("--profile", choices=["leech", "fp16", "bpdq", "trellis", "copy"], default=None)
     return p.parse_args()
 
@@ -55,57 +66,72 @@ def log(msg):
     print("[bench] " + msg, file=sys.stderr, flush=True)
 
 
-def copies_for(nbytes, requested):
-    if requested:
-        return requested
-    return max(2, -(-ROTATE_BYTES // max(nbytes, 1)))
+def cpu_share():
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
 
+
+# ---------------------------------------------------------------- stack workers
+
+def _stack_worker(job):
+    """(layer, matrix) -> the expanded Leech blob of that Qwen3-8B matrix."""
+    import dequant_gemv_lvq_amd as lvq
+    import synth
+    layer, matrix = job
+    d = synth.qwen3_8b_matrix(layer, matrix)
+    blob = lvq.expand(d["coords"], d["scale"], d["tail"], d["rows"], d["cols"])
+    return layer, matrix, d["rows"], d["cols"], blob
+
+
+def start_stack_pool(layers):
+    """Draw and expand the stack in worker processes, forked before the GPU is
+    touched; results stream back while the single-matrix records run."""
+    import multiprocessing as mp
+    import synth
+    jobs = [(li, mi) for li in range(layers) for mi in range(len(synth.QWEN3_8B_MATRICES))]
+    pool = mp.get_context("fork").Pool(cpu_share())
+    return pool, pool.imap_unordered(_stack_worker, jobs, chunksize=1), len(jobs)
+
+
+# ---------------------------------------------------------------- timing
 
 class Timed:
-    """K launches of fn(i) on the current stream, enqueued while the GPU is
-    held busy by a bounded spin kernel (torch.cuda._sleep), so the host's
-    submission time never shows up on the GPU timeline.
-      region_ms:  events around K back-to-back launches (whole-job time)
-      per-launch: a second pass with an event pair around every launch."""
+    """`trials` runs of `steps` back-to-back launches fn(i) on the current
+    stream, each bracketed by events on that stream.  A bounded spin kernel
+    (torch.cuda._sleep) holds the GPU while a trial is enqueued, so host
+    submission never shows on the GPU timeline."""
 
     cycles_per_ms = None
 
-    def __init__(self, torch, fn, steps, warmup):
-        self.torch = torch
+    def __init__(self, torch, fn, steps, warmup, trials, enqueue_ms=0.04):
         for i in range(warmup):
             fn(i)
         torch.cuda.synchronize()
         st = torch.cuda.current_stream()
-        hold = self._hold_cycles(torch, 3.0 + steps * 0.06)
-        r0, r1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda._sleep(hold)
-        r0.record(st)
-        for i in range(steps):
-            fn(i)
-        r1.record(st)
-        torch.cuda.synchronize()
-        self.region_ms = r0.elapsed_time(r1)
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(steps)]
-        torch.cuda._sleep(hold)
-        for i in range(steps):
-            ev[i][0].record(st)
-            fn(i)
-            ev[i][1].record(st)
-        torch.cuda.synchronize()
-        per = sorted(a.elapsed_time(b) for a, b in ev)
-        self.kernel_ms_mean = sum(per) / len(per)
-        self.kernel_ms_median = per[len(per) // 2]
-        self.kernel_ms_min = per[0]
-        self.kernel_ms_max = per[-1]
-        self.steps = steps
+        hold = self._hold_cycles(torch, 2.0 + steps * enqueue_ms)
+        per = []
+        for t in range(trials):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda._sleep(hold)
+            a.record(st)
+            for i in range(steps):
+                fn(t * steps + i)
+            b.record(st)
+            torch.cuda.synchronize()
+            per.append(a.elapsed_time(b) * 1e3 / steps)
+        per.sort()
+        self.us = per
+        self.median = per[len(per) // 2]
 
     @classmethod
     def _hold_cycles(cls, torch, ms):
         if cls.cycles_per_ms is None:
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             n = 1 << 22
-            torch.cuda._sleep(n)  # warm
+            torch.cuda._sleep(n)
             torch.cuda.synchronize()
             a.record()
             torch.cuda._sleep(n)
@@ -115,14 +141,19 @@ class Timed:
         return int(cls.cycles_per_ms * ms)
 
 
-def dev_copies(torch, blob_np, n):
-    """n device copies of a byte blob, each starting on a 256-byte boundary."""
-    nb = blob_np.size
-    stride = (nb + 255) // 256 * 256
+def copies_for(nbytes):
+    return max(2, -(-ROTATE_BYTES // max(nbytes, 1)))
+
+
+def dev_copies(torch, arr, n):
+    """n device copies of a numpy array's bytes, each on a 256-byte boundary."""
+    import numpy as np
+    raw = np.ascontiguousarray(arr).view(np.uint8).reshape(-1)
+    stride = (raw.size + 255) // 256 * 256
     buf = torch.empty((n, stride), dtype=torch.uint8, device="cuda")
-    src = torch.from_numpy(blob_np).to("cuda")
+    src = torch.from_numpy(raw).to("cuda")
     for i in range(n):
-        buf[i, :nb].copy_(src)
+        buf[i, :raw.size].copy_(src)
     return buf
 
 
@@ -154,43 +185,367 @@ def traffic_from_profile():
     return float(t.group(1))
 
 
-# ---------------------------------------------------------------------- arms
+# ---------------------------------------------------------------- algorithmic bytes
 
-def leech_logical_bytes(rows, cols):
-    """Algorithmic weight bytes of the Leech layout: 14 per 24-weight block
-    (16-bit class, 24-bit sign plane, three 24-bit rank planes), 2 per row for
-    the scale and 2 per unquantized tail column."""
+def leech_bytes(rows, cols):
+    """14 B per 24-weight block (16-bit class, sign plane, three rank planes),
+    2 B per row for the scale, 2 B per unquantized tail column."""
     nb, tau = cols // 24, cols % 24
     return rows * (14 * nb + 2 + 2 * tau)
 
 
-def leech_setup(lvq, synth):
-    t0 = time.perf_counter()
-    d = synth.leech_matrix(ROWS, COLS, 4)
-    x = synth.activations(COLS, 1, 4, rows=ROWS)
-    blob = lvq.expand(d["coords"], d["scale"], d["tail"], ROWS, COLS)
-    log("leech workload drawn and expanded in %.1fs" % (time.perf_counter() - t0))
-    return d, x, blob, leech_logical_bytes(ROWS, COLS)
+def bpdq_bytes(rows, cols):
+    return (cols // 16) * rows * 4 + (cols // 256) * 3 * rows * 2
 
 
-def arm_record(tm, nbytes_alg, copies):
-    us = tm.kernel_ms_mean * 1e3
-    gbps = nbytes_alg / (us * 1e-6) / 1e9
-    return {
-        "us_per_gemv": round(us, 3),
-        "us_median": round(tm.kernel_ms_median * 1e3, 3),
-        "us_min": round(tm.kernel_ms_min * 1e3, 3),
-        "us_max": round(tm.kernel_ms_max * 1e3, 3),
-        "gbps": round(gbps, 1),
-        "pct_hbm_peak": round(100 * gbps / HBM_PEAK_GBS, 2),
-        "region_us_per_launch": round(tm.region_ms * 1e3 / tm.steps, 3),
-        "weight_bytes": int(nbytes_alg),
-        "copies": copies,
-    }
+def trellis_bytes(rows, cols):
+    return rows * cols // 4 + 2 * rows + 2 * 65536
 
 
-def run_arm(torch, launch, nbytes_alg, copies, steps, warmup):
-    return arm_record(Timed(torch, launch, steps, warmup), nbytes_alg, copies)
+def fp16_bytes(rows, cols):
+    return 2 * rows * cols
+
+
+# ---------------------------------------------------------------- records
+
+class Bench:
+    def __init__(self, torch, lvq, args, props):
+        self.torch, self.lvq, self.args, self.props = torch, lvq, args, props
+        self.sink = torch.zeros(lvq.STREAM_SINK_WORDS, dtype=torch.int32, device="cuda")
+        self.ceiling = {}
+
+    def time(self, fn, steps=None):
+        a = self.args
+        return Timed(self.torch, fn, steps or a.steps, a.warmup, a.trials)
+
+    def stream_ceiling(self, nbytes):
+        """Median µs of lvq_stream_read over nbytes with the same rotation."""
+        if nbytes in self.ceiling:
+            return self.ceiling[nbytes]
+        torch, lvq = self.torch, self.lvq
+        n = copies_for(nbytes)
+        stride = (nbytes + 255) // 256 * 256
+        buf = torch.empty((n, stride), dtype=torch.uint8, device="cuda")
+        buf.fill_(0x5A)
+        nb4 = nbytes // 4 * 4
+        tm = self.time(lambda i: lvq.stream_read(buf[i % n], nb4, self.sink))
+        del buf
+        self.ceiling[nbytes] = tm.median
+        return tm.median
+
+    def record(self, arm, cfg, rows, cols, batch, nbytes, copies, tm, **extra):
+        us = tm.median
+        gbps = nbytes / (us * 1e-6) / 1e9
+        ceil = self.stream_ceiling(nbytes)
+        r = {
+            "arm": arm, "cfg": cfg, "R": rows, "K": cols, "batch": batch,
+            "bytes_weights": int(nbytes), "bytes_x": 2 * cols * batch, "bytes_y": 4 * rows * batch,
+            "bits_per_weight": round(8.0 * nbytes / (rows * cols), 4),
+            "us_median": round(us, 3), "us_min": round(tm.us[0], 3), "us_max": round(tm.us[-1], 3),
+            "gbps": round(gbps, 1), "pct_hbm_peak": round(100 * gbps / HBM_PEAK_GBS, 2),
+            "stream_ceiling_us": round(ceil, 3), "pct_stream_ceiling": round(100 * ceil / us, 1),
+            "copies": copies, "reps": self.args.steps, "trials": self.args.trials, "graph": False,
+        }
+        r.update(extra)
+        log("%-8s cfg%s %5dx%-5d b%d: %7.3f us  %7.1f GB/s  %5.1f%% peak  %5.1f%% of stream"
+            % (arm, cfg, rows, cols, batch, us, gbps, r["pct_hbm_peak"], r["pct_stream_ceiling"]))
+        return r
+
+    # one Leech matrix at one shape and batch
+    def leech(self, cfg, rows, cols, batch, d=None, keep=False):
+        import synth
+        torch, lvq = self.torch, self.lvq
+        if d is None:
+            d = synth.leech_matrix(rows, cols, cfg)
+        x = synth.activations(cols, batch, cfg, rows=rows)
+        blob = lvq.expand(d["coords"], d["scale"], d["tail"], rows, cols)
+        nbytes = leech_bytes(rows, cols)
+        n = copies_for(blob.size)
+        bufs = dev_copies(torch, blob, n)
+        xd = to_dev(torch, x)
+        yd = torch.empty((batch, rows), dtype=torch.float32, device="cuda")
+        tm = self.time(lambda i: lvq.gemv(bufs[i % n], rows, cols, xd, yd, batch))
+        rec = self.record("leech", cfg, rows, cols, batch, nbytes, n, tm,
+                          blob_bytes=int(blob.size))
+        out = (rec, d, x, yd.cpu().numpy()) if keep else rec
+        if keep:
+            self.graph_us = self.graph(lambda i: lvq.gemv(bufs[i % n], rows, cols, xd, yd, batch))
+        del bufs
+        torch.cuda.empty_cache()
+        return out
+
+    def graph(self, fn):
+        """Median µs per launch of `steps` launches captured in one HIP graph
+        and replayed (the same rotation); None if capture is unavailable."""
+        torch = self.torch
+        steps = self.args.steps
+        try:
+            g = torch.cuda.CUDAGraph()
+            s = torch.cuda.Stream()
+            s.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(s):
+                fn(0)
+                torch.cuda.synchronize()
+                with torch.cuda.graph(g, stream=s):
+                    for i in range(steps):
+                        fn(i)
+            torch.cuda.current_stream().wait_stream(s)
+            torch.cuda.synchronize()
+            per = []
+            for _ in range(self.args.trials):
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record()
+                g.replay()
+                b.record()
+                torch.cuda.synchronize()
+                per.append(a.elapsed_time(b) * 1e3 / steps)
+            per.sort()
+            return round(per[len(per) // 2], 3)
+        except Exception as e:  # graph capture is optional context
+            log("graph capture unavailable: %s" % e)
+            return None
+
+    def fp16(self, cfg, rows, cols, batch):
+        import synth
+        torch, lvq = self.torch, self.lvq
+        wb = synth.dense_matrix(rows, cols, cfg=2)
+        x = synth.activations(cols, batch, 2, rows=rows)
+        nbytes = fp16_bytes(rows, cols)
+        n = copies_for(nbytes)
+        bufs = dev_copies(torch, wb, n)
+        xd = to_dev(torch, x)
+        yd = torch.empty((batch, rows), dtype=torch.float32, device="cuda")
+        tm = self.time(lambda i: lvq.fp16_gemv(bufs[i % n], rows, cols, xd, yd, batch))
+        del bufs
+        torch.cuda.empty_cache()
+        return self.record("fp16", cfg, rows, cols, batch, nbytes, n, tm)
+
+    def bpdq(self, rows, cols, batch):
+        import synth
+        torch, lvq = self.torch, self.lvq
+        d = synth.bpdq_matrix(rows, cols)
+        x = synth.activations(cols, batch, 2, rows=rows)
+        nbytes = bpdq_bytes(rows, cols)
+        n = copies_for(nbytes)
+        codes = dev_copies(torch, d["codes"], n)
+        coeffs = dev_copies(torch, d["coeffs"], n)
+        xd = to_dev(torch, x)
+        yd = torch.empty((batch, rows), dtype=torch.float32, device="cuda")
+        tm = self.time(lambda i: lvq.bpdq_gemv(codes[i % n], coeffs[i % n], rows, cols, xd, yd,
+                                              batch))
+        del codes, coeffs
+        torch.cuda.empty_cache()
+        return self.record("bpdq", 2, rows, cols, batch, nbytes, n, tm)
+
+    def trellis(self, rows, cols, batch):
+        import synth
+        torch, lvq = self.torch, self.lvq
+        d = synth.trellis_matrix(rows, cols)
+        x = synth.activations(cols, batch, 4, rows=rows)
+        nbytes = trellis_bytes(rows, cols)
+        n = copies_for(nbytes)
+        bits = dev_copies(torch, d["bits"], n)
+        table = to_dev(torch, d["table"])
+        scale = to_dev(torch, d["scale"])
+        xd = to_dev(torch, x)
+        yd = torch.empty((batch, rows), dtype=torch.float32, device="cuda")
+        tm = self.time(lambda i: lvq.trellis_gemv(bits[i % n], table, scale, rows, cols, xd, yd,
+                                                 batch))
+        del bits
+        torch.cuda.empty_cache()
+        return self.record("trellis", 4, rows, cols, batch, nbytes, n, tm)
+
+    # the Qwen3-8B stack: 36 layers x 7 Leech GEMVs
+    def load_stack(self, results, njobs):
+        torch = self.torch
+        t0 = time.perf_counter()
+        blobs = {}
+        for li, mi, rows, cols, blob in results:
+            blobs[(li, mi)] = (rows, cols, to_dev(torch, blob))
+        torch.cuda.synchronize()
+        log("stack: %d matrices drawn, expanded and uploaded in %.1fs"
+            % (njobs, time.perf_counter() - t0))
+        return blobs
+
+    def stack(self, blobs, layers):
+        import synth
+        torch, lvq = self.torch, self.lvq
+        total = sum(leech_bytes(r, c) for (r, c, _) in blobs.values())
+        ys = {}
+        for (li, mi), (rows, cols, _) in blobs.items():
+            ys[(li, mi)] = torch.empty((1, rows), dtype=torch.float32, device="cuda")
+
+        def renorm(y):
+            v = y.double()
+            return ((v - v.mean()) / v.std(unbiased=False)).half().view(torch.int16).contiguous()
+
+        def gemv(li, mi, xin):
+            rows, cols, b = blobs[(li, mi)]
+            lvq.gemv(b, rows, cols, xin, ys[(li, mi)], 1)
+            return ys[(li, mi)]
+
+        h0 = to_dev(torch, synth.activations(4096, 1, 5, key=(0,)))
+        inputs = {}
+
+        def chain(record):
+            h = h0
+            for li in range(layers):
+                for mi in (0, 1, 2):
+                    if record:
+                        inputs[(li, mi)] = h
+                    gemv(li, mi, h)
+                xo = renorm(ys[(li, 0)])
+                if record:
+                    inputs[(li, 3)] = xo
+                gemv(li, 3, xo)
+                xg = renorm(ys[(li, 3)])
+                for mi in (4, 5):
+                    if record:
+                        inputs[(li, mi)] = xg
+                    gemv(li, mi, xg)
+                xd = renorm(ys[(li, 5)])
+                if record:
+                    inputs[(li, 6)] = xd
+                gemv(li, 6, xd)
+                h = renorm(ys[(li, 6)])
+            return h
+
+        chain(True)
+        torch.cuda.synchronize()
+        order = [(li, mi) for li in range(layers) for mi in range(7)]
+
+        def gemv_only(_):
+            for li, mi in order:
+                gemv(li, mi, inputs[(li, mi)])
+
+        # host enqueue time per pass: ~252 launches (GEMV only), ~1000 with the
+        # renormalisation ops; the hold covers it
+        tm = Timed(torch, gemv_only, 5, 2, self.args.trials, enqueue_ms=len(order) * 0.02)
+        tc = Timed(torch, lambda _: chain(False), 3, 1, self.args.trials,
+                   enqueue_ms=len(order) * 0.08)
+        us = tm.median  # µs per pass over all GEMVs
+        rec = {
+            "arm": "leech", "cfg": 5, "model": "Qwen3-8B-shaped Leech stack, random init",
+            "layers": layers, "gemvs": len(order),
+            "bytes_weights": int(total), "bits_per_weight": round(
+                8.0 * total / sum(r * c for (r, c, _) in blobs.values()), 4),
+            "us_gemv_only": round(us, 1), "us_min": round(tm.us[0], 1), "us_max": round(tm.us[-1], 1),
+            "gbps": round(total / (us * 1e-6) / 1e9, 1),
+            "pct_hbm_peak": round(100 * total / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 2),
+            "us_chain_with_renorm": round(tc.median, 1),
+            "launches": len(order), "trials": self.args.trials, "graph": False,
+        }
+        log("stack: %d GEMVs %.1f us (%.1f GB/s, %.1f%% peak); chain with renorm %.1f us"
+            % (len(order), us, rec["gbps"], rec["pct_hbm_peak"], tc.median))
+        del blobs, inputs, ys
+        torch.cuda.empty_cache()
+        return rec
+
+
+# ---------------------------------------------------------------- CPU baseline
+
+def cpu_baseline(d, x, y_timed, per_shape):
+    """The oracle as it stands on the host cores: the metric workload for at
+    least 10 s with every core (the reported value), one core and all cores
+    with the reconstruction and the matvec timed apart, and the other config
+    shapes (median of 3 with all cores)."""
+    import numpy as np
+    from threadpoolctl import threadpool_info, threadpool_limits
+    from oracle import gemv as og
+    import synth
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    alg = leech_bytes(ROWS, COLS)
+
+    def phases(dd, xx, cols):
+        t0 = time.perf_counter()
+        w = og.leech_weights(dd["coords"], dd["scale"], dd["tail"], cols)
+        t1 = time.perf_counter()
+        y64, bound = og.gemv(w, xx)
+        t2 = time.perf_counter()
+        return t1 - t0, t2 - t1, y64, bound
+
+    passes, t_cpu = 0, 0.0
+    y64 = bound = None
+    while t_cpu < 10.0 and passes < 200:
+        a, b, y64, bound = phases(d, x, COLS)
+        t_cpu += a + b
+        passes += 1
+    ratio = og.check(y_timed, y64, bound)
+    one = []
+    with threadpool_limits(limits=1):
+        for _ in range(3):
+            one.append(phases(d, x, COLS)[:2])
+    one.sort(key=lambda p: p[0] + p[1])
+    a1, b1 = one[1]
+    many = sorted((phases(d, x, COLS)[:2] for _ in range(3)), key=lambda p: p[0] + p[1])[1]
+    shapes = {}
+    for (cfg, rows, cols) in per_shape:
+        dd = synth.leech_matrix(rows, cols, cfg)
+        xx = synth.activations(cols, 1, cfg, rows=rows)
+        ts = sorted(sum(phases(dd, xx, cols)[:2]) for _ in range(3))
+        shapes["cfg%d_%dx%d" % (cfg, rows, cols)] = round(ts[1] * 1e6, 1)
+    cpu = {"value": round(alg * passes / t_cpu / 1e9, 3), "unit": "GB/s",
+           "cores": int(threads), "kind": "oracle",
+           "sample": "the full 4096x12288 Leech matrix, f64 reconstruction + matvec + per-row "
+                     "bound, %d passes in %.1fs (%.1f ms per GEMV)"
+                     % (passes, t_cpu, 1e3 * t_cpu / passes),
+           "oracle_us_1core": {"reconstruct": round(a1 * 1e6, 1), "matvec": round(b1 * 1e6, 1)},
+           "oracle_us_ncores": {"reconstruct": round(many[0] * 1e6, 1),
+                                "matvec": round(many[1] * 1e6, 1)},
+           "oracle_us_per_shape_ncores": shapes}
+    return cpu, ratio
+
+
+# ---------------------------------------------------------------- main
+
+def profile_only(torch, lvq, args):
+    import synth
+    steps = max(args.steps, 1)
+    if args.profile == "copy":
+        n = 64 << 20
+        a = torch.randn(n, device="cuda", dtype=torch.float32)
+        b = torch.empty(n, device="cuda", dtype=torch.float16)
+        for _ in range(steps):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        log("copy: %d fp32 -> fp16 elements per launch (reads %d B, writes %d B)"
+            % (n, 4 * n, 2 * n))
+        return
+    if args.profile == "leech":
+        d = synth.leech_matrix(ROWS, COLS, 4)
+        blob = lvq.expand(d["coords"], d["scale"], d["tail"], ROWS, COLS)
+        n = copies_for(blob.size)
+        bufs = dev_copies(torch, blob, n)
+        xd = to_dev(torch, synth.activations(COLS, 1, 4, rows=ROWS))
+        yd = torch.empty((1, ROWS), dtype=torch.float32, device="cuda")
+        fn = lambda i: lvq.gemv(bufs[i % n], ROWS, COLS, xd, yd, 1)  # noqa: E731
+    elif args.profile == "fp16":
+        wb = synth.dense_matrix(ROWS, COLS, cfg=2)
+        n = copies_for(wb.size * 2)
+        bufs = dev_copies(torch, wb, n)
+        xd = to_dev(torch, synth.activations(COLS, 1, 2, rows=ROWS))
+        yd = torch.empty((1, ROWS), dtype=torch.float32, device="cuda")
+        fn = lambda i: lvq.fp16_gemv(bufs[i % n], ROWS, COLS, xd, yd, 1)  # noqa: E731
+    elif args.profile == "bpdq":
+        d = synth.bpdq_matrix(4096, 4096)
+        n = copies_for(bpdq_bytes(4096, 4096))
+        codes = dev_copies(torch, d["codes"], n)
+        coeffs = dev_copies(torch, d["coeffs"], n)
+        xd = to_dev(torch, synth.activations(4096, 1, 2, rows=4096))
+        yd = torch.empty((1, 4096), dtype=torch.float32, device="cuda")
+        fn = lambda i: lvq.bpdq_gemv(codes[i % n], coeffs[i % n], 4096, 4096, xd, yd, 1)  # noqa
+    else:
+        d = synth.trellis_matrix(ROWS, COLS)
+        n = copies_for(trellis_bytes(ROWS, COLS))
+        bits = dev_copies(torch, d["bits"], n)
+        table, scale = to_dev(torch, d["table"]), to_dev(torch, d["scale"])
+        xd = to_dev(torch, synth.activations(COLS, 1, 4, rows=ROWS))
+        yd = torch.empty((1, ROWS), dtype=torch.float32, device="cuda")
+        fn = lambda i: lvq.trellis_gemv(bits[i % n], table, scale, ROWS, COLS, xd, yd, 1)  # noqa
+    for i in range(steps):
+        fn(i)
+    torch.cuda.synchronize()
+    log("profile %s: %d launches" % (args.profile, steps))
 
 
 def main():
@@ -200,167 +555,75 @@ def main():
               "(rows would shard with one all-gather of y); run with --gpus 1.",
               file=sys.stderr)
         sys.exit(2)
-    import numpy as np
     import torch
 
     import dequant_gemv_lvq_amd as lvq
-    import synth
+
+    pool = None
+    if args.profile is None and not args.no_stack and not args.no_arms:
+        pool, stack_results, stack_jobs = start_stack_pool(args.stack_layers)
+        log("stack: drawing %d matrices in %d worker processes" % (stack_jobs, cpu_share()))
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     props = torch.cuda.get_device_properties(0)
-    log("device %s (%s), %d CUs" % (props.name, getattr(props, "gcnArchName", "?"),
-                                    props.multi_processor_count))
-
-    # ------------------------------------------------ plain copy (counter scale)
-    if args.profile == "copy":
-        n = 64 << 20
-        a = torch.randn(n, device="cuda", dtype=torch.float32)
-        b = torch.empty(n, device="cuda", dtype=torch.float16)
-        for _ in range(max(args.steps, 1)):
-            b.copy_(a)
-        torch.cuda.synchronize()
-        log("copy: %d fp32 -> fp16 elements per launch (reads %d B, writes %d B)"
-            % (n, 4 * n, 2 * n))
+    arch = getattr(props, "gcnArchName", "?")
+    log("device %s (%s), %d CUs" % (props.name, arch, props.multi_processor_count))
+    if args.profile:
+        profile_only(torch, lvq, args)
         return
 
-    steps, warmup = args.steps, args.warmup
-    arms = {}
+    B = Bench(torch, lvq, args, props)
+    stack_blobs = None
+    if pool is not None:
+        # the whole stack is drawn and on the device, and the workers are gone,
+        # before anything is timed: busy host cores would slow the enqueueing
+        stack_blobs = B.load_stack(stack_results, stack_jobs)
+        pool.close()
+        pool.join()
+    t0 = time.perf_counter()
+    head, d, x, y_timed = B.leech(4, ROWS, COLS, 1, keep=True)
+    log("headline done in %.1fs" % (time.perf_counter() - t0))
 
-    # ------------------------------------------------ Leech (the step)
-    if args.profile in (None, "leech"):
-        d, x, blob, alg = leech_setup(lvq, synth)
-        n = copies_for(blob.size, args.copies)
-        bufs = dev_copies(torch, blob, n)
-        xd = to_dev(torch, x)
-        yd = torch.empty((1, ROWS), dtype=torch.float32, device="cuda")
+    records = [head]
+    stack = None
+    if not args.no_arms:
+        records.append(B.fp16(4, ROWS, COLS, 1))
+        records.append(B.leech(4, ROWS, COLS, 4, d=d))
+        records.append(B.leech(1, 1536, 1536, 1))
+        records.append(B.bpdq(4096, 4096, 1))
+        records.append(B.bpdq(4096, 4096, 4))
+        records.append(B.fp16(2, 4096, 4096, 1))
+        for rows in (4096, 12288):
+            d3 = __import__("synth").leech_matrix(rows, 4096, 3)
+            records.append(B.leech(3, rows, 4096, 1, d=d3))
+            records.append(B.leech(3, rows, 4096, 4, d=d3))
+        records.append(B.trellis(ROWS, COLS, 1))
+        fp16_by_shape = {(r["R"], r["K"]): r["gbps"] for r in records if r["arm"] == "fp16"}
+        for r in records:
+            c = fp16_by_shape.get((r["R"], r["K"]))
+            r["pct_fp16_control"] = round(100 * r["gbps"] / c, 1) if c and r["arm"] != "fp16" else None
+        if stack_blobs is not None:
+            stack = B.stack(stack_blobs, args.stack_layers)
+            del stack_blobs
 
-        def leech_launch(i):
-            lvq.gemv(bufs[i % n], ROWS, COLS, xd, yd, 1)
-
-        if args.profile == "leech":
-            for i in range(steps):
-                leech_launch(i)
-            torch.cuda.synchronize()
-            log("profile leech: %d launches" % steps)
-            return
-        leech = run_arm(torch, leech_launch, alg, n, steps, warmup)
-        torch.cuda.synchronize()
-        y_timed = yd.cpu().numpy()  # output of the last timed launch
-        leech.update({
-            "bits_per_weight": round(8 * alg / (ROWS * COLS), 4),
-            "blob_bytes": int(blob.size),
-        })
-        arms["leech"] = leech
-        del bufs
-        torch.cuda.empty_cache()
-
-    # ------------------------------------------------ comparison arms
-    if not args.no_arms or args.profile in ("fp16", "bpdq", "trellis"):
-        if args.profile in (None, "fp16"):
-            wb = synth.dense_matrix(ROWS, COLS, cfg=2)
-            xf = synth.activations(COLS, 1, 2, rows=ROWS)
-            nbytes = wb.size * 2
-            n = copies_for(nbytes, 0)
-            buf = torch.empty((n, ROWS * COLS), dtype=torch.int16, device="cuda")
-            src = to_dev(torch, wb.reshape(-1))
-            for i in range(n):
-                buf[i].copy_(src)
-            xd = to_dev(torch, xf)
-            yd = torch.empty((1, ROWS), dtype=torch.float32, device="cuda")
-            fn = lambda i: lvq.fp16_gemv(buf[i % n], ROWS, COLS, xd, yd, 1)  # noqa: E731
-            if args.profile == "fp16":
-                for i in range(steps):
-                    fn(i)
-                torch.cuda.synchronize()
-                return
-            arms["fp16"] = run_arm(torch, fn, nbytes, n, steps, warmup)
-            arms["fp16"]["bits_per_weight"] = 16.0
-            arms["fp16"]["shape"] = [ROWS, COLS]
-            del buf
-            torch.cuda.empty_cache()
-
-        if args.profile in (None, "bpdq"):
-            R2 = K2 = 4096
-            db = synth.bpdq_matrix(R2, K2)
-            xb = synth.activations(K2, 1, 2, rows=R2)
-            nbytes = db["codes"].size * 4 + db["coeffs"].size * 2
-            n = copies_for(nbytes, 0)
-            codes = [to_dev(torch, db["codes"]) for _ in range(n)]
-            coeffs = [to_dev(torch, db["coeffs"]) for _ in range(n)]
-            xd = to_dev(torch, xb)
-            yd = torch.empty((1, R2), dtype=torch.float32, device="cuda")
-            fn = lambda i: lvq.bpdq_gemv(codes[i % n], coeffs[i % n], R2, K2, xd, yd, 1)  # noqa
-            if args.profile == "bpdq":
-                for i in range(steps):
-                    fn(i)
-                torch.cuda.synchronize()
-                return
-            arms["bpdq"] = run_arm(torch, fn, nbytes, n, steps, warmup)
-            arms["bpdq"]["bits_per_weight"] = round(8 * nbytes / (R2 * K2), 4)
-            arms["bpdq"]["shape"] = [R2, K2]
-            del codes, coeffs
-            torch.cuda.empty_cache()
-
-        if args.profile in (None, "trellis"):
-            dt = synth.trellis_matrix(ROWS, COLS)
-            xt = synth.activations(COLS, 1, 4, rows=ROWS)
-            nbytes = dt["bits"].size * 4 + dt["scale"].size * 2 + dt["table"].size * 2
-            n = copies_for(nbytes, 0)
-            bits = [to_dev(torch, dt["bits"]) for _ in range(n)]
-            table = to_dev(torch, dt["table"])
-            scale = to_dev(torch, dt["scale"])
-            xd = to_dev(torch, xt)
-            yd = torch.empty((1, ROWS), dtype=torch.float32, device="cuda")
-            fn = lambda i: lvq.trellis_gemv(bits[i % n], table, scale, ROWS, COLS, xd, yd, 1)  # noqa
-            if args.profile == "trellis":
-                for i in range(steps):
-                    fn(i)
-                torch.cuda.synchronize()
-                return
-            arms["trellis"] = run_arm(torch, fn, nbytes, n, steps, warmup)
-            arms["trellis"]["bits_per_weight"] = round(8 * nbytes / (ROWS * COLS), 4)
-            arms["trellis"]["shape"] = [ROWS, COLS]
-            del bits
-            torch.cuda.empty_cache()
-
-    leech = arms["leech"]
-    if "fp16" in arms:
-        leech["pct_fp16_control"] = round(100 * leech["gbps"] / arms["fp16"]["gbps"], 1)
-
-    # ------------------------------------------------ CPU baseline: the oracle
     cpu = None
     if not args.no_cpu:
-        from oracle import gemv as og
-        try:
-            from threadpoolctl import threadpool_info
-            threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-        except Exception:
-            threads = 1
-        passes, t_cpu = 0, 0.0
-        while t_cpu < 10.0 and passes < 200:
-            t0 = time.perf_counter()
-            w = og.leech_weights(d["coords"], d["scale"], d["tail"], COLS)
-            y64, bound = og.gemv(w, x)
-            t_cpu += time.perf_counter() - t0
-            passes += 1
-            del w
-        leech["parity_max_ratio"] = round(og.check(y_timed, y64, bound), 5)
-        cpu = {"value": round(alg * passes / t_cpu / 1e9, 3), "unit": "GB/s",
-               "cores": int(threads), "kind": "oracle",
-               "sample": "the full 4096x12288 Leech matrix, f64 reconstruction + matvec + "
-                         "per-row bound, %d passes in %.1fs (%.1f ms per GEMV)"
-                         % (passes, t_cpu, 1e3 * t_cpu / passes)}
+        t0 = time.perf_counter()
+        cpu, ratio = cpu_baseline(d, x, y_timed, [(1, 1536, 1536), (3, 4096, 4096),
+                                                  (3, 12288, 4096), (3, 1024, 4096)])
+        head["parity_max_ratio"] = round(ratio, 5)
+        log("cpu baseline done in %.1fs" % (time.perf_counter() - t0))
 
-    value = leech["weight_bytes"] / (leech["region_us_per_launch"] * 1e-6) / 1e9
-    region_gbps = round(value, 1)
+    us = head["us_median"]
+    value = head["bytes_weights"] / (us * 1e-6) / 1e9
     out = {
         "metric": METRIC,
         "value": round(value, 1),
         "unit": "GB/s",
         "n_gpus": 1,
-        "steps": steps,
-        "warmup": warmup,
-        "ms_per_step": round(leech["region_us_per_launch"] / 1e3, 6),
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(us / 1e3, 6),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -368,14 +631,18 @@ def main():
         "data": "synthetic",
         "config": {"workload": "Leech GEMV 4096x12288 (down_proj-shaped), batch 1, "
                                "shells 2..6 with P(m)~2^-m, LP3 layout 4.668 b/w",
-                   "rows": ROWS, "cols": COLS, "batch": 1, "copies": leech["copies"],
-                   "device": props.name, "torch": torch.__version__},
-        "roofline": {"bound": "hbm", "achieved": region_gbps, "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(region_gbps / HBM_PEAK_GBS, 4),
+                   "rows": ROWS, "cols": COLS, "batch": 1, "copies": head["copies"],
+                   "trials": args.trials, "device": props.name, "arch": arch,
+                   "torch": torch.__version__, "hip": getattr(torch.version, "hip", None)},
+        "roofline": {"bound": "hbm", "achieved": round(value, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(value / HBM_PEAK_GBS, 4),
                      "traffic": traffic_from_profile()},
         "cpu_baseline": cpu,
-        "us_per_gemv": leech["us_per_gemv"],
-        "arms": arms,
+        "us_per_gemv": us,
+        "us_per_gemv_graph": getattr(B, "graph_us", None),
+        "pct_stream_ceiling": head["pct_stream_ceiling"],
+        "records": records,
+        "stack": stack,
     }
     print(json.dumps(out))
 

@@ -16,6 +16,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "liblvq.so")
 
 NUM_CLASSES = 302
+STREAM_SINK_WORDS = 4096
 MAX_BATCH = 4
 
 LVQ_OK = 0
@@ -60,6 +61,7 @@ def _load():
         "bpdq_gemv": (i, [vp, vp, i, i, vp, vp, i, vp]),
         "trellis_gemv": (i, [vp, vp, vp, i, i, vp, vp, i, vp]),
         "fp16_gemv": (i, [vp, i, i, vp, vp, i, vp]),
+        "lvq_stream_read": (i, [vp, sz, vp, vp]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -70,7 +72,8 @@ def _load():
 
 _lib = _load()
 EXPORTED = ("lvq_strerror", "lvq_last_error_index", "lvq_class_table", "lvq_layout_bytes",
-            "lvq_expand", "lvq_gemv", "lvq_decode", "bpdq_gemv", "trellis_gemv", "fp16_gemv")
+            "lvq_expand", "lvq_gemv", "lvq_decode", "bpdq_gemv", "trellis_gemv", "fp16_gemv",
+            "lvq_stream_read")
 
 
 def library():
@@ -180,3 +183,9 @@ def trellis_gemv(bits, table, scale, rows: int, cols: int, x, y, batch: int = 1,
 def fp16_gemv(w, rows: int, cols: int, x, y, batch: int = 1, stream=None):
     _check(_lib.fp16_gemv(_ptr(w), int(rows), int(cols), _ptr(x), _ptr(y), int(batch),
                           _stream(stream)))
+
+
+def stream_read(buf, nbytes: int, sink, stream=None):
+    """Measurement hook: read nbytes of buf once; the XOR of the STREAM_SINK_WORDS
+    words of sink (cleared by the caller) is the XOR of the buffer's words."""
+    _check(_lib.lvq_stream_read(_ptr(buf), int(nbytes), _ptr(sink), _stream(stream)))

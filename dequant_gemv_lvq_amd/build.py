@@ -17,7 +17,8 @@ OUT_DIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "liblvq.so")
 ARCH = os.environ.get("LVQ_OFFLOAD_ARCH", "gfx950")
 
-HIP_SOURCES = ["lvq_gemv.hip", "fp16_gemv.hip", "bpdq_gemv.hip", "trellis_gemv.hip"]
+HIP_SOURCES = ["lvq_gemv.hip", "fp16_gemv.hip", "bpdq_gemv.hip", "trellis_gemv.hip",
+               "measure.hip"]
 HOST_SOURCES = ["expand.cpp"]
 
 HIPCC_FLAGS = [

@@ -1,0 +1,71 @@
+// Read-only streaming kernel (lvq_stream_read): the achievable-bandwidth
+// reference the GEMV kernels are compared with.  It reads every byte of a
+// buffer once, with the same 16-byte non-temporal loads and the same grid
+// shape rules as a weight stream, and folds the words into one checksum so
+// the loads cannot be dropped.
+//
+// gfx950 design: 256-thread workgroups, at most eight per CU, grid-strided;
+// each thread keeps four 16-byte loads in flight per trip.  The checksum is
+// the XOR of all 32-bit words (order-free): reduced per wave by shuffles and
+// per workgroup in LDS, then stored by each workgroup into its own sink word
+// (no atomics: many atomics on one cache line serialize in L2 and would time
+// the atomics, not the stream); the checksum is the XOR of the sink words.
+
+#include "common.h"
+
+namespace lvq {
+
+constexpr int kStreamThreads = 256;
+constexpr int kStreamUnroll = 4;
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__global__ void __launch_bounds__(kStreamThreads)
+stream_read_kernel(const u32x4* __restrict__ src, size_t n16, const uint32_t* __restrict__ tail,
+                   int ntail, uint32_t* sink) {
+  const size_t stride = (size_t)gridDim.x * kStreamThreads * kStreamUnroll;
+  uint32_t acc = 0;
+  for (size_t base = (size_t)blockIdx.x * kStreamThreads * kStreamUnroll + threadIdx.x;
+       base < n16; base += stride) {
+    u32x4 v[kStreamUnroll];
+#pragma unroll
+    for (int i = 0; i < kStreamUnroll; ++i) {
+      const size_t idx = base + (size_t)i * kStreamThreads;
+      v[i] = idx < n16 ? __builtin_nontemporal_load(src + idx) : (u32x4){0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int i = 0; i < kStreamUnroll; ++i) acc ^= v[i].x ^ v[i].y ^ v[i].z ^ v[i].w;
+  }
+  if (blockIdx.x == 0 && (int)threadIdx.x < ntail) acc ^= tail[threadIdx.x];
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) acc ^= (uint32_t)__shfl_xor((int)acc, off, kWave);
+  __shared__ uint32_t part[kStreamThreads / kWave];
+  if ((threadIdx.x & (kWave - 1)) == 0) part[threadIdx.x / kWave] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t a = 0;
+#pragma unroll
+    for (int i = 0; i < kStreamThreads / kWave; ++i) a ^= part[i];
+    sink[blockIdx.x] = a;
+  }
+}
+
+}  // namespace lvq
+
+using namespace lvq;
+
+extern "C" int lvq_stream_read(const void* buf, size_t bytes, uint32_t* sink, void* stream) {
+  if (!sink || (bytes && !buf)) return LVQ_E_NULL;
+  if (!aligned16(buf) || ((uintptr_t)sink & 3) || (bytes & 3)) return LVQ_E_ALIGN;
+  const size_t n16 = bytes / 16;
+  const int ntail = (int)((bytes % 16) / 4);
+  size_t wgs = (n16 + (size_t)kStreamThreads * kStreamUnroll - 1) / ((size_t)kStreamThreads * kStreamUnroll);
+  size_t cap = (size_t)device_cus() * 8;
+  if (cap > LVQ_STREAM_SINK_WORDS) cap = LVQ_STREAM_SINK_WORDS;
+  if (wgs > cap) wgs = cap;
+  if (wgs < 1) wgs = 1;
+  clear_hip_error();
+  hipLaunchKernelGGL(stream_read_kernel, dim3((unsigned)wgs), dim3(kStreamThreads), 0,
+                     (hipStream_t)stream, (const u32x4*)buf, n16,
+                     (const uint32_t*)((const uint8_t*)buf + n16 * 16), ntail, sink);
+  return launch_status();
+}

@@ -175,3 +175,7 @@ def test_device_entry_points_validate_before_launch():
     assert lib.trellis_gemv(A, A, A + 2, 16, 256, A, A, 1, None) == lvq.LVQ_E_ALIGN
     assert lib.fp16_gemv(A, 16, 100, A, A, 1, None) == lvq.LVQ_E_SHAPE
     assert lib.fp16_gemv(A, 16, 128, A, None, 1, None) == lvq.LVQ_E_NULL
+    assert lib.lvq_stream_read(None, 64, A, None) == lvq.LVQ_E_NULL
+    assert lib.lvq_stream_read(A, 64, None, None) == lvq.LVQ_E_NULL
+    assert lib.lvq_stream_read(A + 4, 64, A, None) == lvq.LVQ_E_ALIGN
+    assert lib.lvq_stream_read(A, 66, A, None) == lvq.LVQ_E_ALIGN

@@ -196,3 +196,15 @@ def test_trellis_gemv(rows, cols, batch):
     r = og.check(to_host(yd, np.float32), y64, bound)
     _report("trellis %dx%d b%d" % (rows, cols, batch), r)
     assert r <= 1.0
+
+
+# ---------------------------------------------------------------- streaming reference
+
+@pytest.mark.parametrize("nbytes", [4, 20, 4096, 1 << 20, (29368320 // 16) * 16 + 12])
+def test_stream_read_checksum(nbytes):
+    words = np.random.default_rng(nbytes).integers(0, 1 << 32, nbytes // 4, dtype=np.uint64)
+    words = words.astype(np.uint32)
+    sink = to_dev(np.zeros(lvq.STREAM_SINK_WORDS, dtype=np.uint32))
+    lvq.stream_read(to_dev(words), nbytes, sink)
+    got = np.bitwise_xor.reduce(to_host(sink, np.uint32))
+    assert int(got) == int(np.bitwise_xor.reduce(words))
