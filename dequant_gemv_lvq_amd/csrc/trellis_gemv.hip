@@ -8,13 +8,16 @@
 // form a tail-biting packet.
 //
 // gfx950 design.  One 1024-thread workgroup per CU copies the 128 KiB table
-// into LDS once and then loops over rows (one wave per row at a time).  Lane l
-// takes code words l, l + 64, ... of the row; for each of the 16 symbols of
-// its word the state is a single funnel shift (v_alignbit) of the previous
-// and current word, masked to 16 bits, and the weight is one LDS read.  Two
-// table values are packed into an fp16 pair for v_dot2_f32_f16 against the x
-// pair; the row scale is applied after the fixed butterfly reduction.  The
-// previous word of the first word of a packet is the packet's last word.
+// and x into LDS with buffer loads that write LDS directly, then its waves
+// walk rows (one row per wave at a time).  Lane l takes code words l, l + 64,
+// ... of the row; all of them are requested at once, so a row costs one
+// memory round trip.  The word before word w in its packet (w - 1, or the
+// packet's last word for its first word) is held by lane l - 1 or l + 15 and
+// comes over with one lane shuffle.  For each of the 16 symbols of a word the
+// table's byte address (state * 2) is one funnel shift of the previous and
+// current word (v_alignbit) and one mask; the value is one LDS read.  Two
+// table values are packed into an fp16 pair for v_dot2_f32_f16 against the
+// x pair; the row scale is applied after a fixed DPP reduction.
 
 #include "common.h"
 
@@ -22,6 +25,27 @@ namespace lvq {
 
 constexpr int kTrellisThreads = 1024;
 constexpr int kTrellisWaves = kTrellisThreads / kWave;
+constexpr int kTrellisMaxWordsPerLane = 12;  // batch * cols <= 12288: <= 768 words per row
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t trellis_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+
+// byte address in the table of the state after symbol p (0..15) of `cur`,
+// whose predecessor word is `prev`: bits 30-2p .. 45-2p of prev:cur, times 2
+__device__ __forceinline__ uint32_t trellis_addr(uint32_t prev, uint32_t cur, int p) {
+  const uint32_t w = p < 15 ? __builtin_amdgcn_alignbit(prev, cur, 29 - 2 * p) : cur << 1;
+  return w & 0x1FFFEu;
+}
+
+// The kernel declares no static LDS, so its dynamic LDS (the table first)
+// starts at LDS address 0 and a table byte address is an LDS address: reading
+// through it directly saves adding the base to every lookup.
+typedef const _Float16 __attribute__((address_space(3))) lds_f16_t;
+__device__ __forceinline__ lds_f16_t* lds_f16(uint32_t byte_addr) {
+  return (lds_f16_t*)(uintptr_t)byte_addr;
+}
 
 template <int B>
 __global__ void __launch_bounds__(kTrellisThreads)
@@ -29,38 +53,67 @@ trellis_gemv_kernel(const uint32_t* __restrict__ bits, const uint16_t* __restric
                     const uint16_t* __restrict__ scale, int rows, int cols,
                     const uint16_t* __restrict__ x, float* __restrict__ y) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  uint16_t* tbl = (uint16_t*)smem;                 // [65536]
+  // smem: the table fp16 [65536] (byte address 2 * state), then x
   uint32_t* xs = (uint32_t*)(smem + 65536 * 2);    // [B][cols/2] natural-order pairs
   const int tid = threadIdx.x;
-  for (int i = tid; i < 65536 / 8; i += kTrellisThreads)
-    ((uint4*)tbl)[i] = ((const uint4*)table)[i];
-  for (int i = tid; i < B * cols / 8; i += kTrellisThreads)
-    ((uint4*)xs)[i] = ((const uint4*)x)[i];
+  const int lane = tid & (kWave - 1);
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int nw = cols / 16;
+
+  // table and x straight into LDS, 1 KiB per wave instruction
+  {
+    const auto rt = trellis_rsrc(table, 65536 * 2);
+    for (int q = wv; q < 128; q += kTrellisWaves)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rt, (__attribute__((address_space(3))) void*)(smem + q * 1024), 16, lane * 16, q * 1024,
+          0, 0);
+    const int xbytes = B * cols * 2;  // a multiple of 512
+    const auto rx = trellis_rsrc(x, (uint32_t)xbytes);
+    for (int q = wv; q * 1024 < xbytes; q += kTrellisWaves)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rx, (__attribute__((address_space(3))) void*)((uint8_t*)xs + q * 1024), 16, lane * 16,
+          q * 1024, 0, 0);
+  }
   __syncthreads();
 
-  const int nw = cols / 16;
-  const int lane = tid & (kWave - 1);
-  const int wave = blockIdx.x * kTrellisWaves + tid / kWave;
+  const int wave = blockIdx.x * kTrellisWaves + wv;
   const int nwaves = gridDim.x * kTrellisWaves;
+  const int src = (lane & 15) ? lane - 1 : lane + 15;  // holder of the previous word
   for (int r = wave; r < rows; r += nwaves) {
-    const uint32_t* brow = bits + (size_t)r * nw;
+    // every word of the row at once (words past the row's end read 0)
+    const auto rb = trellis_rsrc(bits + (size_t)r * nw, (uint32_t)nw * 4);
+    uint32_t cw[kTrellisMaxWordsPerLane];
+#pragma unroll
+    for (int j = 0; j < kTrellisMaxWordsPerLane; ++j)
+      cw[j] = j * kWave < nw ? __builtin_amdgcn_raw_buffer_load_b32(rb, (lane + j * kWave) * 4, 0, 2)
+                             : 0u;
+    const auto rsc = trellis_rsrc(scale + r, 2);
+    const uint32_t sbits = __builtin_amdgcn_raw_buffer_load_b16(rsc, 0, 0, 0);
     float acc[B][2];
 #pragma unroll
     for (int bb = 0; bb < B; ++bb) acc[bb][0] = acc[bb][1] = 0.f;
-    for (int i = lane; i < nw; i += kWave) {
-      const uint32_t cur = brow[i];
-      const uint32_t prev = brow[(i & 15) ? i - 1 : i + 15];
 #pragma unroll
-      for (int p = 0; p < 16; p += 2) {
-        const uint32_t s0 = __builtin_amdgcn_alignbit(prev, cur, 30 - 2 * p) & 0xFFFFu;
-        const uint32_t s1 = __builtin_amdgcn_alignbit(prev, cur, 28 - 2 * p) & 0xFFFFu;
-        const uint32_t w2 = (uint32_t)tbl[s0] | ((uint32_t)tbl[s1] << 16);
+    for (int j = 0; j < kTrellisMaxWordsPerLane; ++j) {
+      if (j * kWave >= nw) break;                  // uniform
+      const int w = lane + j * kWave;
+      const uint32_t cur = cw[j];
+      const uint32_t prev = (uint32_t)__shfl((int)cur, src, kWave);
+      if (w < nw) {
 #pragma unroll
-        for (int bb = 0; bb < B; ++bb)
-          acc[bb][p >> 3] = dot2(w2, xs[(size_t)bb * (cols / 2) + 8 * i + (p >> 1)], acc[bb][p >> 3]);
+        for (int p = 0; p < 16; p += 2) {
+          // the two table values land in the two halves of one register
+          lvq_half2 h;
+          h.x = *lds_f16(trellis_addr(prev, cur, p));
+          h.y = *lds_f16(trellis_addr(prev, cur, p + 1));
+          const uint32_t w2 = __builtin_bit_cast(uint32_t, h);
+#pragma unroll
+          for (int bb = 0; bb < B; ++bb)
+            acc[bb][(p >> 1) & 1] =
+                dot2(w2, xs[(size_t)bb * (cols / 2) + 8 * w + (p >> 1)], acc[bb][(p >> 1) & 1]);
+        }
       }
     }
-    const float s = (float)__builtin_bit_cast(_Float16, scale[r]);
+    const float s = (float)__builtin_bit_cast(_Float16, (uint16_t)sbits);
 #pragma unroll
     for (int bb = 0; bb < B; ++bb) {
       const float tot = wave_sum_lane63(acc[bb][0] + acc[bb][1]);
@@ -74,7 +127,8 @@ int zero_output(float* y, size_t n, hipStream_t st);
 template <int B>
 int launch_trellis(const uint32_t* bits, const uint16_t* table, const uint16_t* scale, int rows,
                    int cols, const uint16_t* x, float* y, hipStream_t st) {
-  const size_t lds = 65536 * 2 + (size_t)B * cols * 2;
+  // x rounded up to whole KiB: the last buffer-to-LDS copy writes a full KiB
+  const size_t lds = 65536 * 2 + (((size_t)B * cols * 2 + 1023) & ~(size_t)1023);
   if (lds > device_lds_bytes()) return LVQ_E_SHAPE;
   int wgs = (rows + kTrellisWaves - 1) / kTrellisWaves;
   if (wgs > device_cus()) wgs = device_cus();
