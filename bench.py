@@ -247,8 +247,10 @@ class Bench:
             "copies": copies, "reps": self.args.steps, "trials": self.args.trials, "graph": False,
         }
         r.update(extra)
-        log("%-8s cfg%s %5dx%-5d b%d: %7.3f us  %7.1f GB/s  %5.1f%% peak  %5.1f%% of stream"
-            % (arm, cfg, rows, cols, batch, us, gbps, r["pct_hbm_peak"], r["pct_stream_ceiling"]))
+        log("%-8s cfg%s %5dx%-5d b%d: %7.3f us  %7.1f GB/s  %5.1f%% peak  %5.1f%% of stream%s"
+            % (arm, cfg, rows, cols, batch, us, gbps, r["pct_hbm_peak"], r["pct_stream_ceiling"],
+               "" if "us_noweights" not in extra else "  (no weights %.3f us)"
+               % extra["us_noweights"]))
         return r
 
     # one Leech matrix at one shape and batch
@@ -265,8 +267,12 @@ class Bench:
         xd = to_dev(torch, x)
         yd = torch.empty((batch, rows), dtype=torch.float32, device="cuda")
         tm = self.time(lambda i: lvq.gemv(bufs[i % n], rows, cols, xd, yd, batch))
+        # the no-weights control: the same launch reading no weight bytes
+        y0 = torch.empty_like(yd)
+        t0 = self.time(lambda i: lvq.gemv_noweights(bufs[i % n], rows, cols, xd, y0, batch))
         rec = self.record("leech", cfg, rows, cols, batch, nbytes, n, tm,
-                          blob_bytes=int(blob.size))
+                          blob_bytes=int(blob.size), us_noweights=round(t0.median, 3),
+                          pct_time_noweights=round(100 * t0.median / tm.median, 1))
         out = (rec, d, x, yd.cpu().numpy()) if keep else rec
         if keep:
             self.graph_us = self.graph(lambda i: lvq.gemv(bufs[i % n], rows, cols, xd, yd, batch))
@@ -418,9 +424,40 @@ class Bench:
             for li, mi in order:
                 gemv(li, mi, inputs[(li, mi)])
 
+        # q/k/v share their input, and so do gate/up: one launch each
+        groups = []
+        for li in range(layers):
+            groups += [(li, (0, 1, 2)), (li, (3,)), (li, (4, 5)), (li, (6,))]
+        fused_args = []
+        for li, mis in groups:
+            cols = blobs[(li, mis[0])][1]
+            fused_args.append(([blobs[(li, mi)][2] for mi in mis],
+                               [blobs[(li, mi)][0] for mi in mis], cols, inputs[(li, mis[0])],
+                               [ys[(li, mi)] for mi in mis]))
+
+        def fused_only(_):
+            for a in fused_args:
+                lvq.gemv_fused(*a, 1)
+
+        def noweights_only(_):
+            for li, mi in order:
+                rows, cols, b = blobs[(li, mi)]
+                lvq.gemv_noweights(b, rows, cols, inputs[(li, mi)], ys[(li, mi)], 1)
+
+        gemv_only(0)
+        torch.cuda.synchronize()
+        y_sep = {k: v.clone() for k, v in ys.items()}
+        fused_only(0)
+        torch.cuda.synchronize()
+        fused_same = all(torch.equal(ys[k].view(torch.int32), y_sep[k].view(torch.int32))
+                         for k in ys)
+        del y_sep
+
         # host enqueue time per pass: ~252 launches (GEMV only), ~1000 with the
         # renormalisation ops; the hold covers it
         tm = Timed(torch, gemv_only, 5, 2, self.args.trials, enqueue_ms=len(order) * 0.02)
+        tf = Timed(torch, fused_only, 5, 2, self.args.trials, enqueue_ms=len(groups) * 0.08)
+        t0 = Timed(torch, noweights_only, 5, 2, self.args.trials, enqueue_ms=len(order) * 0.02)
         tc = Timed(torch, lambda _: chain(False), 3, 1, self.args.trials,
                    enqueue_ms=len(order) * 0.08)
         us = tm.median  # µs per pass over all GEMVs
@@ -434,9 +471,16 @@ class Bench:
             "pct_hbm_peak": round(100 * total / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 2),
             "us_chain_with_renorm": round(tc.median, 1),
             "launches": len(order), "trials": self.args.trials, "graph": False,
+            "us_fused": round(tf.median, 1), "launches_fused": len(groups),
+            "fused_speedup": round(us / tf.median, 4), "fused_bit_equal": bool(fused_same),
+            "gbps_fused": round(total / (tf.median * 1e-6) / 1e9, 1),
+            "us_noweights": round(t0.median, 1),
+            "pct_time_noweights": round(100 * t0.median / us, 1),
         }
         log("stack: %d GEMVs %.1f us (%.1f GB/s, %.1f%% peak); chain with renorm %.1f us"
             % (len(order), us, rec["gbps"], rec["pct_hbm_peak"], tc.median))
+        log("stack: fused %d launches %.1f us (x%.3f, bit-equal %s); no-weights %.1f us"
+            % (len(groups), tf.median, rec["fused_speedup"], fused_same, t0.median))
         del blobs, inputs, ys
         torch.cuda.empty_cache()
         return rec

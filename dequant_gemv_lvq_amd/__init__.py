@@ -17,6 +17,7 @@ LIB_PATH = os.path.join(_HERE, "liblvq.so")
 
 NUM_CLASSES = 302
 STREAM_SINK_WORDS = 4096
+MAX_FUSED = 4
 MAX_BATCH = 4
 
 LVQ_OK = 0
@@ -57,6 +58,8 @@ def _load():
         "lvq_layout_bytes": (sz, [i, i]),
         "lvq_expand": (i, [vp, vp, vp, i, i, vp]),
         "lvq_gemv": (i, [vp, i, i, vp, vp, i, vp]),
+        "lvq_gemv_fused": (i, [i, vp, vp, i, vp, vp, i, vp]),
+        "lvq_gemv_noweights": (i, [vp, i, i, vp, vp, i, vp]),
         "lvq_decode": (i, [vp, i, i, vp, vp]),
         "bpdq_gemv": (i, [vp, vp, i, i, vp, vp, i, vp]),
         "trellis_gemv": (i, [vp, vp, vp, i, i, vp, vp, i, vp]),
@@ -72,8 +75,8 @@ def _load():
 
 _lib = _load()
 EXPORTED = ("lvq_strerror", "lvq_last_error_index", "lvq_class_table", "lvq_layout_bytes",
-            "lvq_expand", "lvq_gemv", "lvq_decode", "bpdq_gemv", "trellis_gemv", "fp16_gemv",
-            "lvq_stream_read")
+            "lvq_expand", "lvq_gemv", "lvq_gemv_fused", "lvq_gemv_noweights", "lvq_decode",
+            "bpdq_gemv", "trellis_gemv", "fp16_gemv", "lvq_stream_read")
 
 
 def library():
@@ -164,6 +167,25 @@ def last_error_index():
 def gemv(blob, rows: int, cols: int, x, y, batch: int = 1, stream=None):
     _check(_lib.lvq_gemv(_ptr(blob), int(rows), int(cols), _ptr(x), _ptr(y), int(batch),
                          _stream(stream)))
+
+
+def gemv_fused(blobs, rows, cols: int, x, ys, batch: int = 1, stream=None):
+    """One launch for len(blobs) matrices sharing x: ys[m] = W_m x."""
+    n = len(blobs)
+    if len(rows) != n or len(ys) != n:
+        raise ValueError("blobs, rows and ys must have the same length")
+    bp = (ctypes.c_void_p * max(n, 1))(*[_ptr(b) for b in blobs])
+    rp = (ctypes.c_int * max(n, 1))(*[int(r) for r in rows])
+    yp = (ctypes.c_void_p * max(n, 1))(*[_ptr(y) for y in ys])
+    _check(_lib.lvq_gemv_fused(int(n), bp, rp, int(cols), _ptr(x), yp, int(batch),
+                               _stream(stream)))
+
+
+def gemv_noweights(blob, rows: int, cols: int, x, y, batch: int = 1, stream=None):
+    """No-weights control: lvq_gemv's launch for this shape reading no weight
+    bytes (y = 0); blob only supplies the class table."""
+    _check(_lib.lvq_gemv_noweights(_ptr(blob), int(rows), int(cols), _ptr(x), _ptr(y),
+                                   int(batch), _stream(stream)))
 
 
 def decode(blob, rows: int, cols: int, out, stream=None):

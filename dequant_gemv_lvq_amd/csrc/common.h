@@ -94,9 +94,6 @@ __device__ __forceinline__ uint32_t leech_pair(uint32_t word, int v, uint32_t lu
   return __builtin_amdgcn_perm(lut_hi, lut_lo, r & 0x08070807u);
 }
 
-// Code word of an origin block (every slot 1, every flag set): decodes to +0.
-constexpr uint32_t kZeroWord = 0x99999999u;
-
 // LUT words of a class-table entry (bytes 0..4 ascending magnitudes).
 __device__ __forceinline__ uint2 leech_lut(uint64_t entry) {
   uint2 l;

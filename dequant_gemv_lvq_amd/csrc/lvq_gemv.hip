@@ -116,6 +116,55 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, 
 // not evict x, the class table or the row scales)
 constexpr int kStream = 2;
 
+// The matrices one launch works on: one (lvq_gemv, lvq_gemv_noweights) or up
+// to kMaxFused sharing x and the column count (lvq_gemv_fused), their rows
+// concatenated: global row g belongs to matrix m when start[m] <= g <
+// start[m + 1].  Kernel modes: single matrix, fused set, and the no-weights
+// control (the single-matrix launch with every weight load replaced by a
+// register constant: it reads x and writes y, and no weight byte).
+constexpr int kMaxFused = 4;
+constexpr int kSingle = 0, kFused = 1, kNoWeights = 2;
+
+struct MatSet {
+  LeechView v[kMaxFused];
+  float* y[kMaxFused];
+  int start[kMaxFused + 1];
+};
+
+template <int M>
+__device__ __forceinline__ int mat_of(const MatSet& ms, int g) {
+  int m = 0;
+  if (M == kFused) {
+#pragma unroll
+    for (int i = 1; i < kMaxFused; ++i) m += g >= ms.start[i] ? 1 : 0;
+  }
+  return m;
+}
+
+// field f of matrix m, for a wave-uniform m, by scalar selects (a runtime
+// index into the kernel-argument arrays, or a select of whole structs, would
+// copy the arguments to scratch memory)
+template <int M, typename F>
+__device__ __forceinline__ auto pick(const MatSet& ms, int m, F f) {
+  auto r = f(ms, 0);
+  if (M == kFused) {
+#pragma unroll
+    for (int i = 1; i < kMaxFused; ++i) r = m == i ? f(ms, i) : r;
+  }
+  return r;
+}
+
+// start[m] for a wave-uniform m, by selects (indexing the kernel-argument
+// array with a runtime index would copy it to scratch memory)
+// (every mode: with one matrix m is 0 and start_of(ms, 1) is its row count)
+template <int M>
+__device__ __forceinline__ int start_of(const MatSet& ms, int m) {
+  int r = ms.start[0];
+#pragma unroll
+  for (int i = 1; i <= kMaxFused; ++i) r = m == i ? ms.start[i] : r;
+  return r;
+}
+
 // Work item = (row, chunk): a chunk is up to 64 * BPL consecutive blocks of a
 // row, lane l taking blocks chunk0 + l, chunk0 + l + 64, ...  Wave w owns rows
 // w, w + W, w + 2W, ... (W waves in the grid) and walks their chunks in order;
@@ -135,28 +184,46 @@ struct ItemRegs {
 
 // An item's loads come in two groups: its metadata (class ids, this lane's
 // tail value, the row scale: everything the table lookups and the epilogue
-// need) and its code words.
-template <int BPL>
-__device__ __forceinline__ void load_meta(const LeechView& v, int nb, int tau, int r, int chunk,
+// need) and its code words.  In the no-weights mode every load is issued
+// against an empty range: out of range, it returns 0 and sends no request to
+// memory, so the instructions, waits and registers are those of the real
+// kernel and no weight byte is read (0 decodes as class 0, scale 0: y = +0).
+template <int M>
+__device__ __forceinline__ uint32_t weight_bytes(uint32_t n) {
+  return M == kNoWeights ? 0u : n;
+}
+
+template <int BPL, int M>
+__device__ __forceinline__ void load_meta(const MatSet& ms, int nb, int tau, int gr, int chunk,
                                           int lane, ItemRegs<BPL>& g) {
+  const int m = mat_of<M>(ms, gr);
+  const int r = gr - start_of<M>(ms, m);
+  const uint16_t* cls = pick<M>(ms, m, [](const MatSet& s, int i) { return s.v[i].cls; });
+  const uint16_t* tail = pick<M>(ms, m, [](const MatSet& s, int i) { return s.v[i].tail; });
+  const uint16_t* scale = pick<M>(ms, m, [](const MatSet& s, int i) { return s.v[i].scale; });
   const int k0 = chunk * (kWave * BPL);
-  const auto rc = buffer_rsrc(v.cls + (size_t)r * nb + k0, (uint32_t)(nb - k0) * 2);
+  const auto rc =
+      buffer_rsrc(cls + (size_t)r * nb + k0, weight_bytes<M>((uint32_t)(nb - k0) * 2));
 #pragma unroll
   for (int u = 0; u < BPL; ++u)
     g.c[u] = __builtin_amdgcn_raw_buffer_load_b16(rc, (lane + u * kWave) * 2, 0, kStream);
-  const auto rt = buffer_rsrc(v.tail + (size_t)r * tau, (uint32_t)tau * 2);
+  const auto rt = buffer_rsrc(tail + (size_t)r * tau, weight_bytes<M>((uint32_t)tau * 2));
   g.tail = __builtin_amdgcn_raw_buffer_load_b16(rt, lane * 2, 0, 0);
   // the row scale, read by every lane (one transaction); a vector load, so
   // that waiting for it never holds up the LDS reads
-  const auto rs = buffer_rsrc(v.scale + r, 2);
+  const auto rs = buffer_rsrc(scale + r, weight_bytes<M>(2));
   g.scale = __builtin_amdgcn_raw_buffer_load_b16(rs, 0, 0, 0);
 }
 
-template <int BPL>
-__device__ __forceinline__ void load_codes(const LeechView& v, int nb, int r, int chunk, int lane,
+template <int BPL, int M>
+__device__ __forceinline__ void load_codes(const MatSet& ms, int nb, int gr, int chunk, int lane,
                                            ItemRegs<BPL>& g) {
+  const int m = mat_of<M>(ms, gr);
+  const int r = gr - start_of<M>(ms, m);
+  const uint32_t* codes = pick<M>(ms, m, [](const MatSet& s, int i) { return s.v[i].codes; });
   const int k0 = chunk * (kWave * BPL);
-  const auto rw = buffer_rsrc(v.codes + ((size_t)r * nb + k0) * 3, (uint32_t)(nb - k0) * 12);
+  const auto rw = buffer_rsrc(codes + ((size_t)r * nb + k0) * 3,
+                              weight_bytes<M>((uint32_t)(nb - k0) * 12));
 #pragma unroll
   for (int u = 0; u < BPL; ++u) {
     const int o = (lane + u * kWave) * 12;
@@ -167,23 +234,28 @@ __device__ __forceinline__ void load_codes(const LeechView& v, int nb, int r, in
 }
 
 // Both groups, metadata first, so a table lookup never waits for code words.
-template <int BPL>
-__device__ __forceinline__ void load_item(const LeechView& v, int nb, int tau, int r, int chunk,
+template <int BPL, int M>
+__device__ __forceinline__ void load_item(const MatSet& ms, int nb, int tau, int gr, int chunk,
                                           int lane, ItemRegs<BPL>& g) {
-  load_meta<BPL>(v, nb, tau, r, chunk, lane, g);
-  load_codes<BPL>(v, nb, r, chunk, lane, g);
+  load_meta<BPL, M>(ms, nb, tau, gr, chunk, lane, g);
+  load_codes<BPL, M>(ms, nb, gr, chunk, lane, g);
 }
 
 // LDS layout (dynamic): lut uint2[302] | x fp16 [B][kpad], kpad >= 24 * npad and
 // >= cols, a multiple of 512, with npad = nchunks * 64 * BPL blocks; columns past
 // cols are zero.  The 32-bit pair feeding view v of code word w of block k is
 // element 12k + 4w + v of a batch row (natural column order).
-template <int B, int BPL>
-__device__ __forceinline__ void decode_item(int rows, int nb, int tau, int nchunks, int kpad,
-                                            int r, int chunk, int lane, const ItemRegs<BPL>& g,
-                                            const uint2* lut, const uint32_t* xs,
-                                            float (&acc)[B][2], float* __restrict__ y) {
+template <int B, int BPL, int M>
+__device__ __forceinline__ void decode_item(const MatSet& ms, int nb, int tau, int nchunks,
+                                            int kpad, int gr, int chunk, int lane,
+                                            const ItemRegs<BPL>& g, const uint2* lut,
+                                            const uint32_t* xs, float (&acc)[B][3]) {
   asm volatile("" ::: "memory");  // keep this item's LDS reads inside this item
+  // Word wi of every block goes to accumulator wi: consecutive words always
+  // use different registers, and each lane adds its blocks in column order
+  // into the same registers whatever the blocks-per-lane of the launch, so a
+  // row's result does not depend on the launch geometry (or on which other
+  // matrices share the launch).
   const int npair = kpad / 2;
   const uint32_t* xl = xs + (chunk * (kWave * BPL) + lane) * 12;
 #pragma unroll
@@ -197,7 +269,7 @@ __device__ __forceinline__ void decode_item(int rows, int nb, int tau, int nchun
 #pragma unroll
       for (int bb = 0; bb < B; ++bb) {
         const uint4 xq = *(const uint4*)(xl + bb * npair + u * (kWave * 12) + 4 * wi);
-        float& a = acc[bb][(u + wi) & 1];
+        float& a = acc[bb][wi];
         a = dot2(d[0], xq.x, a);
         a = dot2(d[1], xq.y, a);
         a = dot2(d[2], xq.z, a);
@@ -211,13 +283,18 @@ __device__ __forceinline__ void decode_item(int rows, int nb, int tau, int nchun
     const uint16_t* xh = (const uint16_t*)xs;
 #pragma unroll
     for (int bb = 0; bb < B; ++bb) {
-      float part = (acc[bb][0] + acc[bb][1]) * s;
+      float part = (acc[bb][0] + acc[bb][1] + acc[bb][2]) * s;
       if (lane < tau)
         part += half_bits_to_float((uint16_t)g.tail) *
                 half_bits_to_float(xh[bb * kpad + 24 * nb + lane]);
       const float tot = wave_sum_lane63(part);
-      if (lane == kWave - 1) y[(size_t)bb * rows + r] = tot;
-      acc[bb][0] = acc[bb][1] = 0.f;
+      if (lane == kWave - 1) {
+        const int m = mat_of<M>(ms, gr);
+        const int s0 = start_of<M>(ms, m);
+        const int rows_m = start_of<M>(ms, m + 1) - s0;
+        pick<M>(ms, m, [](const MatSet& s, int i) { return s.y[i]; })[(size_t)bb * rows_m + (gr - s0)] = tot;
+      }
+      acc[bb][0] = acc[bb][1] = acc[bb][2] = 0.f;
     }
   }
   asm volatile("" ::: "memory");
@@ -232,10 +309,16 @@ __device__ __forceinline__ uint2 stage_lut(int c, uint64_t entry) {
   return l;
 }
 
-template <int B, int BPL>
+// Waves per SIMD the register allocation must leave room for: 8 (at most 64
+// VGPRs, two 1024-thread workgroups per CU) for the variants that fit there
+// without spilling, and whatever the allocation gives for the larger ones.
+constexpr int leech_min_waves(int B, int BPL) { return B + BPL <= 4 ? 8 : 1; }
+
+template <int B, int BPL, int M>
 __global__ void __launch_bounds__(kMaxWgThreads)
-leech_gemv_kernel(LeechView v, int rows, int nb, int tau, int cols, int nchunks, int kpad,
-                  const uint16_t* __restrict__ x, float* __restrict__ y) {
+__attribute__((amdgpu_waves_per_eu(leech_min_waves(B, BPL))))
+leech_gemv_kernel(MatSet ms, int rows, int nb, int tau, int cols, int nchunks, int kpad,
+                  const uint16_t* __restrict__ x) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   uint2* lut = (uint2*)smem;
   uint32_t* xs = (uint32_t*)(smem + LVQ_NUM_CLASSES * 8);
@@ -274,7 +357,8 @@ leech_gemv_kernel(LeechView v, int rows, int nb, int tau, int cols, int nchunks,
       xh[i] = c < cols ? x[(size_t)bb * cols + c] : (uint16_t)0;
     }
   }
-  const uint64_t te = v.table[min(tid, LVQ_NUM_CLASSES - 1)];
+  const uint64_t* table = ms.v[0].table;  // the same universal table in every blob
+  const uint64_t te = table[min(tid, LVQ_NUM_CLASSES - 1)];
   asm volatile("" ::: "memory");
   // 2. the first two items (a wave with fewer items loads rows it never
   //    uses, so that the load sequence has no branches and every later wait
@@ -283,16 +367,16 @@ leech_gemv_kernel(LeechView v, int rows, int nb, int tau, int cols, int nchunks,
   int ra = wave < rows ? wave : 0, ca = 0;
   int rb = ca + 1 == nchunks ? ra + nwaves : ra, cb = ca + 1 == nchunks ? 0 : ca + 1;
   if (items < 2) { rb = ra; cb = ca; }
-  load_item<BPL>(v, nb, tau, ra, ca, lane, ia);
-  load_item<BPL>(v, nb, tau, rb, cb, lane, ib);
+  load_item<BPL, M>(ms, nb, tau, ra, ca, lane, ia);
+  load_item<BPL, M>(ms, nb, tau, rb, cb, lane, ib);
   asm volatile("" ::: "memory");
   // 3. the class table into LDS; the barrier also waits for x
-  for (int c = tid; c < LVQ_NUM_CLASSES; c += nthr) lut[c] = stage_lut(c, c == tid ? te : v.table[c]);
+  for (int c = tid; c < LVQ_NUM_CLASSES; c += nthr) lut[c] = stage_lut(c, c == tid ? te : table[c]);
   __syncthreads();
 
-  float acc[B][2];
+  float acc[B][3];
 #pragma unroll
-  for (int bb = 0; bb < B; ++bb) acc[bb][0] = acc[bb][1] = 0.f;
+  for (int bb = 0; bb < B; ++bb) acc[bb][0] = acc[bb][1] = acc[bb][2] = 0.f;
   if (items == 0) return;
   // steady state, two items per trip with the register sets ia and ib: decode
   // one while the other and the next one are in flight
@@ -305,23 +389,23 @@ leech_gemv_kernel(LeechView v, int rows, int nb, int tau, int cols, int nchunks,
   };
   int j = 0;
   for (; j + 3 < items; j += 2) {
-    decode_item<B, BPL>(rows, nb, tau, nchunks, kpad, ra, ca, lane, ia, lut, xs, acc, y);
+    decode_item<B, BPL, M>(ms, nb, tau, nchunks, kpad, ra, ca, lane, ia, lut, xs, acc);
     advance(ra, ca);
-    load_item<BPL>(v, nb, tau, ra, ca, lane, ia);
-    decode_item<B, BPL>(rows, nb, tau, nchunks, kpad, rb, cb, lane, ib, lut, xs, acc, y);
+    load_item<BPL, M>(ms, nb, tau, ra, ca, lane, ia);
+    decode_item<B, BPL, M>(ms, nb, tau, nchunks, kpad, rb, cb, lane, ib, lut, xs, acc);
     advance(rb, cb);
-    load_item<BPL>(v, nb, tau, rb, cb, lane, ib);
+    load_item<BPL, M>(ms, nb, tau, rb, cb, lane, ib);
   }
   // the last one to three items
-  decode_item<B, BPL>(rows, nb, tau, nchunks, kpad, ra, ca, lane, ia, lut, xs, acc, y);
+  decode_item<B, BPL, M>(ms, nb, tau, nchunks, kpad, ra, ca, lane, ia, lut, xs, acc);
   if (j + 2 < items) {
     advance(ra, ca);
-    load_item<BPL>(v, nb, tau, ra, ca, lane, ia);
+    load_item<BPL, M>(ms, nb, tau, ra, ca, lane, ia);
   }
   if (j + 1 < items)
-    decode_item<B, BPL>(rows, nb, tau, nchunks, kpad, rb, cb, lane, ib, lut, xs, acc, y);
+    decode_item<B, BPL, M>(ms, nb, tau, nchunks, kpad, rb, cb, lane, ib, lut, xs, acc);
   if (j + 2 < items)
-    decode_item<B, BPL>(rows, nb, tau, nchunks, kpad, ra, ca, lane, ia, lut, xs, acc, y);
+    decode_item<B, BPL, M>(ms, nb, tau, nchunks, kpad, ra, ca, lane, ia, lut, xs, acc);
 }
 
 // Rows shorter than one block: y = sum of the unquantized tail only.
@@ -404,9 +488,8 @@ int zero_output(float* y, size_t n, hipStream_t st) {
   return launch_status();
 }
 
-template <int B, int BPL>
-int launch_leech_bpl(const LeechView& v, int rows, int cols, const uint16_t* x, float* y,
-                     hipStream_t st) {
+template <int B, int BPL, int M>
+int launch_leech_mode(const MatSet& ms, int rows, int cols, const uint16_t* x, hipStream_t st) {
   const int nb = cols / 24, tau = cols % 24;
   const int nchunks = (nb + kWave * BPL - 1) / (kWave * BPL);
   const size_t npad = (size_t)nchunks * kWave * BPL;
@@ -423,8 +506,8 @@ int launch_leech_bpl(const LeechView& v, int rows, int cols, const uint16_t* x, 
   const int ti = threads == 1024 ? 0 : threads == 512 ? 1 : 2, li = lds > 64 * 1024;
   if (!occupancy[ti][li]) {
     int n = 1;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, leech_gemv_kernel<B, BPL>, threads, lds) !=
-            hipSuccess || n < 1)
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, leech_gemv_kernel<B, BPL, M>, threads,
+                                                     lds) != hipSuccess || n < 1)
       n = 1;
     occupancy[ti][li] = n > 2 ? 2 : n;
   }
@@ -432,38 +515,65 @@ int launch_leech_bpl(const LeechView& v, int rows, int cols, const uint16_t* x, 
   if (wgs > (long long)occupancy[ti][li] * cus) wgs = (long long)occupancy[ti][li] * cus;
   if (wgs < 1) wgs = 1;
   clear_hip_error();
-  hipLaunchKernelGGL((leech_gemv_kernel<B, BPL>), dim3((unsigned)wgs), dim3(threads), lds, st, v,
-                     rows, nb, tau, cols, nchunks, (int)kpad, x, y);
+  hipLaunchKernelGGL((leech_gemv_kernel<B, BPL, M>), dim3((unsigned)wgs), dim3(threads), lds, st,
+                     ms, rows, nb, tau, cols, nchunks, (int)kpad, x);
   return launch_status();
 }
 
+template <int B, int BPL>
+int launch_leech_bpl(const MatSet& ms, int mode, int rows, int cols, const uint16_t* x,
+                     hipStream_t st) {
+  if (mode == kFused) return launch_leech_mode<B, BPL, kFused>(ms, rows, cols, x, st);
+  if (mode == kNoWeights) return launch_leech_mode<B, BPL, kNoWeights>(ms, rows, cols, x, st);
+  return launch_leech_mode<B, BPL, kSingle>(ms, rows, cols, x, st);
+}
+
+// rows = total rows of the set; rows shorter than one block go to the
+// tail-only kernel, one launch per matrix
 template <int B>
-int launch_leech(const LeechView& v, int rows, int cols, const uint16_t* x, float* y,
+int launch_leech(const MatSet& ms, int n, int mode, int rows, int cols, const uint16_t* x,
                  hipStream_t st) {
   const int nb = cols / 24;
   if (nb == 0) {
-    clear_hip_error();
-    hipLaunchKernelGGL(leech_tail_only_kernel<B>, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0,
-                       st, v, rows, cols, x, y);
-    return launch_status();
+    for (int m = 0; m < n; ++m) {
+      const int rm = ms.start[m + 1] - ms.start[m];
+      if (!rm) continue;
+      if (mode == kNoWeights) {  // the only weights are the tail: none are read
+        const int e = zero_output(ms.y[m], (size_t)B * rm, st);
+        if (e) return e;
+        continue;
+      }
+      clear_hip_error();
+      hipLaunchKernelGGL(leech_tail_only_kernel<B>, dim3((unsigned)((rm + 255) / 256)), dim3(256),
+                         0, st, ms.v[m], rm, cols, x, ms.y[m]);
+      const int e = launch_status();
+      if (e) return e;
+    }
+    return LVQ_OK;
   }
   const int bpl = choose_bpl(nb, max_bpl(B), rows, device_cus());
   if constexpr (max_bpl(B) >= 4) {
-    if (bpl == 4) return launch_leech_bpl<B, 4>(v, rows, cols, x, y, st);
+    if (bpl == 4) return launch_leech_bpl<B, 4>(ms, mode, rows, cols, x, st);
   }
   if constexpr (max_bpl(B) >= 3) {
-    if (bpl == 3) return launch_leech_bpl<B, 3>(v, rows, cols, x, y, st);
+    if (bpl == 3) return launch_leech_bpl<B, 3>(ms, mode, rows, cols, x, st);
   }
-  if (bpl == 2) return launch_leech_bpl<B, 2>(v, rows, cols, x, y, st);
-  return launch_leech_bpl<B, 1>(v, rows, cols, x, y, st);
+  if (bpl == 2) return launch_leech_bpl<B, 2>(ms, mode, rows, cols, x, st);
+  return launch_leech_bpl<B, 1>(ms, mode, rows, cols, x, st);
 }
 
-}  // namespace lvq
+int launch_set(const MatSet& ms, int n, int mode, int rows, int cols, const uint16_t* x, int batch,
+               hipStream_t st) {
+  switch (batch) {
+    case 1: return launch_leech<1>(ms, n, mode, rows, cols, x, st);
+    case 2: return launch_leech<2>(ms, n, mode, rows, cols, x, st);
+    case 3: return launch_leech<3>(ms, n, mode, rows, cols, x, st);
+    default: return launch_leech<4>(ms, n, mode, rows, cols, x, st);
+  }
+}
 
-using namespace lvq;
-
-extern "C" int lvq_gemv(const void* blob, int rows, int cols, const uint16_t* x, float* y,
-                        int batch, void* stream) {
+int single_gemv(const void* blob, int rows, int cols, const uint16_t* x, float* y, int batch,
+                void* stream, int mode) {
   if (rows < 0 || cols < 0) return LVQ_E_SHAPE;
   int e = check_batch(batch);
   if (e) return e;
@@ -473,13 +583,62 @@ extern "C" int lvq_gemv(const void* blob, int rows, int cols, const uint16_t* x,
   hipStream_t st = (hipStream_t)stream;
   if (rows == 0) return LVQ_OK;
   if (cols == 0) return zero_output(y, (size_t)batch * rows, st);
-  const LeechView v = leech_view(blob, (size_t)rows, (size_t)cols);
-  switch (batch) {
-    case 1: return launch_leech<1>(v, rows, cols, x, y, st);
-    case 2: return launch_leech<2>(v, rows, cols, x, y, st);
-    case 3: return launch_leech<3>(v, rows, cols, x, y, st);
-    default: return launch_leech<4>(v, rows, cols, x, y, st);
+  MatSet ms = {};
+  ms.v[0] = leech_view(blob, (size_t)rows, (size_t)cols);
+  ms.y[0] = y;
+  ms.start[0] = 0;
+  for (int i = 1; i <= kMaxFused; ++i) ms.start[i] = rows;
+  return launch_set(ms, 1, mode, rows, cols, x, batch, st);
+}
+
+}  // namespace lvq
+
+using namespace lvq;
+
+extern "C" int lvq_gemv(const void* blob, int rows, int cols, const uint16_t* x, float* y,
+                        int batch, void* stream) {
+  return single_gemv(blob, rows, cols, x, y, batch, stream, kSingle);
+}
+
+extern "C" int lvq_gemv_noweights(const void* blob, int rows, int cols, const uint16_t* x,
+                                  float* y, int batch, void* stream) {
+  return single_gemv(blob, rows, cols, x, y, batch, stream, kNoWeights);
+}
+
+extern "C" int lvq_gemv_fused(int n, const void* const* blobs, const int* rows, int cols,
+                              const uint16_t* x, float* const* y, int batch, void* stream) {
+  if (n < 1 || n > kMaxFused) return LVQ_E_SHAPE;
+  if (!blobs || !rows || !y) return LVQ_E_NULL;
+  if (cols < 0) return LVQ_E_SHAPE;
+  int e = check_batch(batch);
+  if (e) return e;
+  if ((long long)batch * cols > 65536) return LVQ_E_SHAPE;
+  if (cols && !x) return LVQ_E_NULL;
+  if (!aligned16(x)) return LVQ_E_ALIGN;
+  MatSet ms = {};
+  long long total = 0;
+  for (int m = 0; m < n; ++m) {
+    if (rows[m] < 0) return LVQ_E_SHAPE;
+    if (!blobs[m] || !y[m]) return LVQ_E_NULL;
+    if (!aligned16(blobs[m]) || !aligned16(y[m])) return LVQ_E_ALIGN;
+    ms.v[m] = leech_view(blobs[m], (size_t)rows[m], (size_t)cols);
+    ms.y[m] = y[m];
+    ms.start[m] = (int)total;
+    total += rows[m];
   }
+  if (total > 0x7FFFFFFF) return LVQ_E_SHAPE;
+  for (int m = n; m <= kMaxFused; ++m) ms.start[m] = (int)total;
+  for (int m = n; m < kMaxFused; ++m) { ms.v[m] = ms.v[0]; ms.y[m] = ms.y[0]; }
+  hipStream_t st = (hipStream_t)stream;
+  if (total == 0) return LVQ_OK;
+  if (cols == 0) {
+    for (int m = 0; m < n; ++m) {
+      const int ze = zero_output(y[m], (size_t)batch * rows[m], st);
+      if (ze) return ze;
+    }
+    return LVQ_OK;
+  }
+  return launch_set(ms, n, kFused, (int)total, cols, x, batch, st);
 }
 
 extern "C" int lvq_decode(const void* blob, int rows, int cols, int8_t* coords_out,

@@ -179,3 +179,50 @@ def test_device_entry_points_validate_before_launch():
     assert lib.lvq_stream_read(A, 64, None, None) == lvq.LVQ_E_NULL
     assert lib.lvq_stream_read(A + 4, 64, A, None) == lvq.LVQ_E_ALIGN
     assert lib.lvq_stream_read(A, 66, A, None) == lvq.LVQ_E_ALIGN
+
+
+def test_fused_and_noweights_validate_before_launch():
+    import ctypes
+    lib = lvq.library()
+    A = 1 << 20
+
+    def arr(t, vals):
+        return (t * len(vals))(*vals)
+
+    vp, ci = ctypes.c_void_p, ctypes.c_int
+    blobs, ys = arr(vp, [A, A, A]), arr(vp, [A, A, A])
+    rows = arr(ci, [4, 8, 12])
+    f = lib.lvq_gemv_fused
+    assert f(0, blobs, rows, 48, A, ys, 1, None) == lvq.LVQ_E_SHAPE
+    assert f(lvq.MAX_FUSED + 1, arr(vp, [A] * 5), arr(ci, [4] * 5), 48, A, arr(vp, [A] * 5), 1,
+             None) == lvq.LVQ_E_SHAPE
+    assert f(3, None, rows, 48, A, ys, 1, None) == lvq.LVQ_E_NULL
+    assert f(3, blobs, None, 48, A, ys, 1, None) == lvq.LVQ_E_NULL
+    assert f(3, blobs, rows, 48, A, None, 1, None) == lvq.LVQ_E_NULL
+    assert f(3, arr(vp, [A, None, A]), rows, 48, A, ys, 1, None) == lvq.LVQ_E_NULL
+    assert f(3, blobs, rows, 48, A, arr(vp, [A, A, None]), 1, None) == lvq.LVQ_E_NULL
+    assert f(3, blobs, rows, 48, None, ys, 1, None) == lvq.LVQ_E_NULL
+    assert f(3, arr(vp, [A, A + 8, A]), rows, 48, A, ys, 1, None) == lvq.LVQ_E_ALIGN
+    assert f(3, blobs, rows, 48, A, arr(vp, [A + 4, A, A]), 1, None) == lvq.LVQ_E_ALIGN
+    assert f(3, blobs, rows, 48, A + 2, ys, 1, None) == lvq.LVQ_E_ALIGN
+    assert f(3, blobs, arr(ci, [4, -1, 12]), 48, A, ys, 1, None) == lvq.LVQ_E_SHAPE
+    assert f(3, blobs, rows, -24, A, ys, 1, None) == lvq.LVQ_E_SHAPE
+    assert f(3, blobs, rows, 70000, A, ys, 1, None) == lvq.LVQ_E_SHAPE
+    assert f(3, blobs, rows, 48, A, ys, 0, None) == lvq.LVQ_E_BATCH
+    assert f(3, blobs, rows, 48, A, ys, 5, None) == lvq.LVQ_E_BATCH
+    # more rows in the set than an int indexes
+    assert f(2, blobs, arr(ci, [1 << 30, 1 << 30]), 48, A, ys, 1, None) == lvq.LVQ_E_SHAPE
+    assert f(3, blobs, arr(ci, [0, 0, 0]), 48, A, ys, 1, None) == lvq.LVQ_OK  # nothing to do
+    with pytest.raises(ValueError):
+        lvq.gemv_fused([A, A], [4], 48, A, [A, A])
+    with pytest.raises(lvq.LvqError):
+        lvq.gemv_fused([], [], 48, A, [])
+
+    g = lib.lvq_gemv_noweights
+    assert g(A, 4, 48, A, A, 0, None) == lvq.LVQ_E_BATCH
+    assert g(None, 4, 48, A, A, 1, None) == lvq.LVQ_E_NULL
+    assert g(A, 4, 48, A, None, 1, None) == lvq.LVQ_E_NULL
+    assert g(A + 4, 4, 48, A, A, 1, None) == lvq.LVQ_E_ALIGN
+    assert g(A, -1, 48, A, A, 1, None) == lvq.LVQ_E_SHAPE
+    assert g(A, 4, 70000, A, A, 1, None) == lvq.LVQ_E_SHAPE
+    assert g(A, 0, 48, A, A, 1, None) == lvq.LVQ_OK
