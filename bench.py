@@ -58,7 +58,7 @@ def parse():
     p.add_argument("--no-stack", action="store_true")
     p.add_argument("--no-cpu", action="store_true")
     p.add_argument("--stack-layers", type=int, default=QWEN_LAYERS)
-    p.add_argument("--profile", choices=["leech", "fp16", "bpdq", "trellis", "copy"], default=None)
+    p.add_argument("--profile", choices=["leech", "noweights", "fp16", "bpdq", "trellis", "copy"], default=None)
     return p.parse_args()
 
 
@@ -555,14 +555,15 @@ def profile_only(torch, lvq, args):
         log("copy: %d fp32 -> fp16 elements per launch (reads %d B, writes %d B)"
             % (n, 4 * n, 2 * n))
         return
-    if args.profile == "leech":
+    if args.profile in ("leech", "noweights"):
         d = synth.leech_matrix(ROWS, COLS, 4)
         blob = lvq.expand(d["coords"], d["scale"], d["tail"], ROWS, COLS)
         n = copies_for(blob.size)
         bufs = dev_copies(torch, blob, n)
         xd = to_dev(torch, synth.activations(COLS, 1, 4, rows=ROWS))
         yd = torch.empty((1, ROWS), dtype=torch.float32, device="cuda")
-        fn = lambda i: lvq.gemv(bufs[i % n], ROWS, COLS, xd, yd, 1)  # noqa: E731
+        call = lvq.gemv if args.profile == "leech" else lvq.gemv_noweights
+        fn = lambda i: call(bufs[i % n], ROWS, COLS, xd, yd, 1)  # noqa: E731
     elif args.profile == "fp16":
         wb = synth.dense_matrix(ROWS, COLS, cfg=2)
         n = copies_for(wb.size * 2)
