@@ -361,6 +361,26 @@ class Bench:
         torch.cuda.empty_cache()
         return self.record("trellis", 4, rows, cols, batch, nbytes, n, tm)
 
+    def rotate(self, n, m, batch):
+        """The activation rotation (H kron Q)(S x) at width n = K m."""
+        import numpy as np
+        torch, lvq = self.torch, self.lvq
+        rng = np.random.default_rng(n + m)
+        x = (rng.standard_normal((batch, n)) * 0.5).astype(np.float16).view(np.uint16)
+        words = rng.integers(0, 1 << 32, (n + 31) // 32, dtype=np.uint64).astype(np.uint32)
+        q = np.linalg.qr(rng.standard_normal((m, m)))[0].astype(np.float32) if m > 1 else None
+        xd, wd = to_dev(torch, x), to_dev(torch, words)
+        qd = None if q is None else torch.from_numpy(q).cuda()
+        yd = torch.empty((batch, n), dtype=torch.int16, device="cuda")
+        tm = self.time(lambda i: lvq.rotate(xd, n, m, wd, qd, yd, batch))
+        us = tm.median
+        rec = {"arm": "rotate", "N": n, "m": m, "batch": batch,
+               "bytes": 4 * n * batch, "us_median": round(us, 3),
+               "us_min": round(tm.us[0], 3), "us_max": round(tm.us[-1], 3),
+               "reps": self.args.steps, "trials": self.args.trials}
+        log("rotate   n=%5d m=%2d b%d: %7.3f us" % (n, m, batch, us))
+        return rec
+
     # the Qwen3-8B stack: 36 layers x 7 Leech GEMVs
     def load_stack(self, results, njobs):
         torch = self.torch
@@ -643,8 +663,13 @@ def main():
             records.append(B.leech(3, rows, 4096, 1, d=d3))
             records.append(B.leech(3, rows, 4096, 4, d=d3))
         records.append(B.trellis(ROWS, COLS, 1))
+        for n, m in ((4096, 1), (12288, 3), (25600, 25)):
+            records.append(B.rotate(n, m, 1))
+        records.append(B.rotate(12288, 3, 4))
         fp16_by_shape = {(r["R"], r["K"]): r["gbps"] for r in records if r["arm"] == "fp16"}
         for r in records:
+            if "R" not in r:
+                continue
             c = fp16_by_shape.get((r["R"], r["K"]))
             r["pct_fp16_control"] = round(100 * r["gbps"] / c, 1) if c and r["arm"] != "fp16" else None
         if stack_blobs is not None:

@@ -47,7 +47,7 @@ def _load():
     except ImportError:
         pass
     if not os.path.exists(LIB_PATH):
-        raise ImportError("liblvq.so is not built (%s); run python -m dequant_gemv_lvq_amd.build"
+        raise ImportError("liblvq.so is not built (%s); run python dequant_gemv_lvq_amd/build.py"
                           % LIB_PATH)
     lib = ctypes.CDLL(LIB_PATH)
     vp, i, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
@@ -64,6 +64,7 @@ def _load():
         "bpdq_gemv": (i, [vp, vp, i, i, vp, vp, i, vp]),
         "trellis_gemv": (i, [vp, vp, vp, i, i, vp, vp, i, vp]),
         "fp16_gemv": (i, [vp, i, i, vp, vp, i, vp]),
+        "lvq_rotate": (i, [vp, vp, vp, i, i, vp, i, vp]),
         "lvq_stream_read": (i, [vp, sz, vp, vp]),
     }
     for name, (res, args) in sig.items():
@@ -76,7 +77,7 @@ def _load():
 _lib = _load()
 EXPORTED = ("lvq_strerror", "lvq_last_error_index", "lvq_class_table", "lvq_layout_bytes",
             "lvq_expand", "lvq_gemv", "lvq_gemv_fused", "lvq_gemv_noweights", "lvq_decode",
-            "bpdq_gemv", "trellis_gemv", "fp16_gemv", "lvq_stream_read")
+            "bpdq_gemv", "trellis_gemv", "fp16_gemv", "lvq_rotate", "lvq_stream_read")
 
 
 def library():
@@ -205,6 +206,12 @@ def trellis_gemv(bits, table, scale, rows: int, cols: int, x, y, batch: int = 1,
 def fp16_gemv(w, rows: int, cols: int, x, y, batch: int = 1, stream=None):
     _check(_lib.fp16_gemv(_ptr(w), int(rows), int(cols), _ptr(x), _ptr(y), int(batch),
                           _stream(stream)))
+
+
+def rotate(x, n: int, m: int, sign_words, q, y, batch: int = 1, stream=None):
+    """y = (H kron Q)(S x) per batch row (fp16 in, fp16 out; y may be x)."""
+    _check(_lib.lvq_rotate(_ptr(x), _ptr(sign_words), _ptr(q), int(n), int(m), _ptr(y),
+                           int(batch), _stream(stream)))
 
 
 def stream_read(buf, nbytes: int, sink, stream=None):

@@ -1,6 +1,9 @@
 """Build liblvq.so in-tree: hipcc for the gfx950 kernels, g++ for the host expander.
 
-    python -m dequant_gemv_lvq_amd.build        # or dequant_gemv_lvq_amd.build.build()
+    python dequant_gemv_lvq_amd/build.py        # or __graft_entry__.build()
+
+(Run it as a file: importing it through the package would first load the
+library it is about to build.)
 
 Objects go to dequant_gemv_lvq_amd/_build/, the library to
 dequant_gemv_lvq_amd/liblvq.so.  Every call recompiles.
@@ -18,7 +21,7 @@ LIB = os.path.join(HERE, "liblvq.so")
 ARCH = os.environ.get("LVQ_OFFLOAD_ARCH", "gfx950")
 
 HIP_SOURCES = ["lvq_gemv.hip", "fp16_gemv.hip", "bpdq_gemv.hip", "trellis_gemv.hip",
-               "measure.hip"]
+               "rotate.hip", "measure.hip"]
 HOST_SOURCES = ["expand.cpp"]
 
 HIPCC_FLAGS = [

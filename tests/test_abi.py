@@ -226,3 +226,23 @@ def test_fused_and_noweights_validate_before_launch():
     assert g(A, -1, 48, A, A, 1, None) == lvq.LVQ_E_SHAPE
     assert g(A, 4, 70000, A, A, 1, None) == lvq.LVQ_E_SHAPE
     assert g(A, 0, 48, A, A, 1, None) == lvq.LVQ_OK
+
+
+def test_rotate_validates_before_launch():
+    lib = lvq.library()
+    A = 1 << 20
+    r = lib.lvq_rotate
+    assert r(A, None, None, 4096, 1, A, 0, None) == lvq.LVQ_E_BATCH
+    assert r(A, None, None, -8, 1, A, 1, None) == lvq.LVQ_E_SHAPE
+    assert r(A, None, None, 4096, 0, A, 1, None) == lvq.LVQ_E_SHAPE
+    assert r(A, None, None, 33 * 64, 33, A, 1, None) == lvq.LVQ_E_SHAPE   # m > 32
+    assert r(A, None, None, 100, 3, A, 1, None) == lvq.LVQ_E_SHAPE       # n % m
+    assert r(A, None, None, 3 * 12, 3, A, 1, None) == lvq.LVQ_E_SHAPE    # K = 12
+    assert r(None, None, None, 4096, 1, A, 1, None) == lvq.LVQ_E_NULL
+    assert r(A, None, None, 4096, 1, None, 1, None) == lvq.LVQ_E_NULL
+    assert r(A + 2, None, None, 4096, 1, A, 1, None) == lvq.LVQ_E_ALIGN
+    assert r(A, A + 4, None, 4096, 1, A, 1, None) == lvq.LVQ_E_ALIGN
+    assert r(A, None, A + 8, 3 * 1024, 3, A, 1, None) == lvq.LVQ_E_ALIGN
+    assert r(A, None, None, 0, 1, A, 1, None) == lvq.LVQ_OK              # nothing to do
+    # m > 1: y must not overlap x (the m workgroups of a row all read x)
+    assert r(A, None, None, 3 * 1024, 3, A, 1, None) == lvq.LVQ_E_SHAPE
