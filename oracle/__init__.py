@@ -20,6 +20,8 @@ gemv    f64 reconstruction of W for every arm (Leech, BPDQ, bitshift trellis,
 layout  the expected logical planes of a Leech block and an independent
         unpacker of the packed blob the expander writes.
 rotate  the activation rotation (H kron Q)(S x) with its error bound.
+index   the 47-bit rank / unrank of the m <= 12 ball, the 48-bit word and
+        shape-gain dequantisation.
 
 Parity status: every function is pinned by a CPU test against a value the
 pages print, a classical closed form, or brute force; the exceptions are
