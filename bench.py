@@ -361,6 +361,47 @@ class Bench:
         torch.cuda.empty_cache()
         return self.record("trellis", 4, rows, cols, batch, nbytes, n, tm)
 
+    def unfold(self, nblocks):
+        """Load-time unfolding of random 48-bit words (one per 24-weight block)."""
+        import numpy as np
+        torch, lvq = self.torch, self.lvq
+        rng = np.random.default_rng(nblocks)
+        ball = 111_043_117_458_001
+        words = (rng.integers(0, ball, nblocks, dtype=np.int64).astype(np.uint64) |
+                 (rng.integers(0, 2, nblocks).astype(np.uint64) << np.uint64(47)))
+        wd = torch.from_numpy(words.view(np.int64)).cuda()
+        cd = torch.empty((nblocks, 24), dtype=torch.int8, device="cuda")
+        gd = torch.empty(nblocks, dtype=torch.uint8, device="cuda")
+        lvq.unfold(wd, nblocks, cd, gd)  # uploads the tables once
+        torch.cuda.synchronize()
+        tm = Timed(torch, lambda i: lvq.unfold(wd, nblocks, cd, gd), 20, 3, self.args.trials)
+        us = tm.median
+        rec = {"arm": "unfold", "blocks": nblocks, "weights": 24 * nblocks,
+               "us_median": round(us, 1), "us_min": round(tm.us[0], 1),
+               "gblocks_per_s": round(nblocks / (us * 1e-6) / 1e9, 3),
+               "bytes_in": 8 * nblocks, "bytes_out": 25 * nblocks, "trials": self.args.trials}
+        log("unfold   %d blocks: %.1f us (%.3f G blocks/s)" % (nblocks, us, rec["gblocks_per_s"]))
+        return rec
+
+    def leech_gain(self, rows, cols, batch):
+        """The shape-gain GEMV at one shape (random gain bits, two gain levels)."""
+        import numpy as np
+        import synth
+        torch, lvq = self.torch, self.lvq
+        d = synth.leech_matrix(rows, cols, 4)
+        g = np.random.default_rng(rows).integers(0, 2, (rows, cols // 24)).astype(np.uint8)
+        blob = lvq.expand_gain(d["coords"], g, d["scale"], d["tail"], rows, cols)
+        x = synth.activations(cols, batch, 4, rows=rows)
+        n = copies_for(blob.size)
+        bufs = dev_copies(torch, blob, n)
+        xd = to_dev(torch, x)
+        yd = torch.empty((batch, rows), dtype=torch.float32, device="cuda")
+        tm = self.time(lambda i: lvq.gemv_gain(bufs[i % n], rows, cols, 0.8125, 1.1875, xd, yd,
+                                               batch))
+        del bufs
+        torch.cuda.empty_cache()
+        return self.record("leech_gain", 4, rows, cols, batch, leech_bytes(rows, cols), n, tm)
+
     def rotate(self, n, m, batch):
         """The activation rotation (H kron Q)(S x) at width n = K m."""
         import numpy as np
@@ -666,6 +707,8 @@ def main():
         for n, m in ((4096, 1), (12288, 3), (25600, 25)):
             records.append(B.rotate(n, m, 1))
         records.append(B.rotate(12288, 3, 4))
+        records.append(B.leech_gain(ROWS, COLS, 1))
+        records.append(B.unfold(ROWS * (COLS // 24)))
         fp16_by_shape = {(r["R"], r["K"]): r["gbps"] for r in records if r["arm"] == "fp16"}
         for r in records:
             if "R" not in r:

@@ -57,6 +57,10 @@ def _load():
         "lvq_class_table": (i, [vp]),
         "lvq_layout_bytes": (sz, [i, i]),
         "lvq_expand": (i, [vp, vp, vp, i, i, vp]),
+        "lvq_expand_gain": (i, [vp, vp, vp, vp, i, i, vp]),
+        "lvq_rank": (i, [vp, sz, vp]),
+        "lvq_unfold": (i, [vp, sz, vp, vp, vp]),
+        "lvq_gemv_gain": (i, [vp, i, i, ctypes.c_float, ctypes.c_float, vp, vp, i, vp]),
         "lvq_gemv": (i, [vp, i, i, vp, vp, i, vp]),
         "lvq_gemv_fused": (i, [i, vp, vp, i, vp, vp, i, vp]),
         "lvq_gemv_noweights": (i, [vp, i, i, vp, vp, i, vp]),
@@ -76,7 +80,8 @@ def _load():
 
 _lib = _load()
 EXPORTED = ("lvq_strerror", "lvq_last_error_index", "lvq_class_table", "lvq_layout_bytes",
-            "lvq_expand", "lvq_gemv", "lvq_gemv_fused", "lvq_gemv_noweights", "lvq_decode",
+            "lvq_expand", "lvq_expand_gain", "lvq_rank", "lvq_gemv", "lvq_gemv_gain",
+            "lvq_unfold", "lvq_gemv_fused", "lvq_gemv_noweights", "lvq_decode",
             "bpdq_gemv", "trellis_gemv", "fp16_gemv", "lvq_rotate", "lvq_stream_read")
 
 
@@ -157,6 +162,34 @@ def expand(coords, scale, tail, rows: int, cols: int) -> np.ndarray:
     return blob
 
 
+def expand_gain(coords, gain_bits, scale, tail, rows: int, cols: int) -> np.ndarray:
+    """lvq_expand with a shape-gain bit per block (uint8 [rows][cols//24])."""
+    coords = np.ascontiguousarray(coords, dtype=np.int8)
+    gain_bits = np.ascontiguousarray(gain_bits, dtype=np.uint8)
+    scale = np.ascontiguousarray(scale, dtype=np.uint16)
+    tau = cols % 24
+    tail = None if tau == 0 else np.ascontiguousarray(tail, dtype=np.uint16)
+    if rows < 0 or cols < 0 or gain_bits.size != rows * (cols // 24):
+        _check(LVQ_E_SHAPE)
+    blob = np.empty(_lib.lvq_layout_bytes(int(rows), int(cols)), dtype=np.uint8)
+    code = _lib.lvq_expand_gain(_ptr(coords), _ptr(gain_bits), _ptr(scale), _ptr(tail),
+                                int(rows), int(cols), blob.ctypes.data)
+    if code != LVQ_OK:
+        r, b = ctypes.c_int(), ctypes.c_int()
+        _lib.lvq_last_error_index(ctypes.byref(r), ctypes.byref(b))
+        _check(code, (r.value, b.value))
+    return blob
+
+
+def rank(coords) -> np.ndarray:
+    """47-bit index of each block: int8 [..., 24] -> uint64 [...]."""
+    coords = np.ascontiguousarray(coords, dtype=np.int8)
+    n = coords.size // 24
+    out = np.empty(n, dtype=np.uint64)
+    _check(_lib.lvq_rank(_ptr(coords), n, out.ctypes.data))
+    return out.reshape(coords.shape[:-1])
+
+
 def last_error_index():
     r, b = ctypes.c_int(), ctypes.c_int()
     _check(_lib.lvq_last_error_index(ctypes.byref(r), ctypes.byref(b)))
@@ -187,6 +220,19 @@ def gemv_noweights(blob, rows: int, cols: int, x, y, batch: int = 1, stream=None
     bytes (y = 0); blob only supplies the class table."""
     _check(_lib.lvq_gemv_noweights(_ptr(blob), int(rows), int(cols), _ptr(x), _ptr(y),
                                    int(batch), _stream(stream)))
+
+
+def gemv_gain(blob, rows: int, cols: int, gain0: float, gain1: float, x, y, batch: int = 1,
+              stream=None):
+    _check(_lib.lvq_gemv_gain(_ptr(blob), int(rows), int(cols), float(gain0), float(gain1),
+                              _ptr(x), _ptr(y), int(batch), _stream(stream)))
+
+
+def unfold(words, nblocks: int, coords_out, gain_out, stream=None):
+    """48-bit words (device uint64) -> coordinates int8 [n][24] and gain bits
+    (0xFF marks an invalid word)."""
+    _check(_lib.lvq_unfold(_ptr(words), int(nblocks), _ptr(coords_out), _ptr(gain_out),
+                           _stream(stream)))
 
 
 def decode(blob, rows: int, cols: int, out, stream=None):

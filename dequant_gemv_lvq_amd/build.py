@@ -21,8 +21,8 @@ LIB = os.path.join(HERE, "liblvq.so")
 ARCH = os.environ.get("LVQ_OFFLOAD_ARCH", "gfx950")
 
 HIP_SOURCES = ["lvq_gemv.hip", "fp16_gemv.hip", "bpdq_gemv.hip", "trellis_gemv.hip",
-               "rotate.hip", "measure.hip"]
-HOST_SOURCES = ["expand.cpp"]
+               "rotate.hip", "unfold.hip", "measure.hip"]
+HOST_SOURCES = ["expand.cpp", "index.cpp"]
 
 HIPCC_FLAGS = [
     "-O3", "-std=c++17", "-fPIC", "--offload-arch=" + ARCH,

@@ -207,6 +207,11 @@ const ClassTable& table() {
 
 }  // namespace
 
+namespace {
+int expand_impl(const int8_t* coords, const uint8_t* gain_bits, const uint16_t* scale,
+                const uint16_t* tail, int rows, int cols, void* blob_out);
+}  // namespace
+
 extern "C" {
 
 const char* lvq_strerror(int code) {
@@ -245,6 +250,21 @@ size_t lvq_layout_bytes(int rows, int cols) {
 
 int lvq_expand(const int8_t* coords, const uint16_t* scale, const uint16_t* tail, int rows,
                int cols, void* blob_out) {
+  return expand_impl(coords, nullptr, scale, tail, rows, cols, blob_out);
+}
+
+int lvq_expand_gain(const int8_t* coords, const uint8_t* gain_bits, const uint16_t* scale,
+                    const uint16_t* tail, int rows, int cols, void* blob_out) {
+  if (rows > 0 && cols >= 24 && !gain_bits) return LVQ_E_NULL;
+  return expand_impl(coords, gain_bits, scale, tail, rows, cols, blob_out);
+}
+
+}  // extern "C"
+
+namespace {
+
+int expand_impl(const int8_t* coords, const uint8_t* gain_bits, const uint16_t* scale,
+                const uint16_t* tail, int rows, int cols, void* blob_out) {
   g_err_row = g_err_block = -1;
   if (rows < 0 || cols < 0) return LVQ_E_SHAPE;
   const size_t R = (size_t)rows, nb = (size_t)cols / 24, tau = (size_t)cols % 24;
@@ -304,7 +324,16 @@ int lvq_expand(const int8_t* coords, const uint16_t* scale, const uint16_t* tail
         if (v >= 0) w[j >> 3] |= 1u << ((4 * n + 11) & 31);
       }
       std::memcpy(codes + (r * nb + k) * 3, w, 12);
-      cls[r * nb + k] = (uint16_t)id;
+      uint16_t g = 0;
+      if (gain_bits) {
+        if (gain_bits[r * nb + k] > 1) {
+          g_err_row = (int)r;
+          g_err_block = (int)k;
+          return LVQ_E_SHAPE;
+        }
+        g = (uint16_t)(gain_bits[r * nb + k] << 15);
+      }
+      cls[r * nb + k] = (uint16_t)(id | g);
     }
   }
   if (R) std::memcpy(out + s.scale, scale, R * 2);
@@ -312,4 +341,4 @@ int lvq_expand(const int8_t* coords, const uint16_t* scale, const uint16_t* tail
   return LVQ_OK;
 }
 
-}  // extern "C"
+}  // namespace

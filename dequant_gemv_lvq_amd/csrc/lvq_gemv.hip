@@ -123,12 +123,15 @@ constexpr int kStream = 2;
 // control (the single-matrix launch with every weight load replaced by a
 // register constant: it reads x and writes y, and no weight byte).
 constexpr int kMaxFused = 4;
-constexpr int kSingle = 0, kFused = 1, kNoWeights = 2;
+// kGain: one matrix whose class ids carry a shape-gain bit in bit 15; the
+// block's weights are multiplied by gain[bit]
+constexpr int kSingle = 0, kFused = 1, kNoWeights = 2, kGain = 3;
 
 struct MatSet {
   LeechView v[kMaxFused];
   float* y[kMaxFused];
   int start[kMaxFused + 1];
+  float gain[2];
 };
 
 template <int M>
@@ -260,7 +263,9 @@ __device__ __forceinline__ void decode_item(const MatSet& ms, int nb, int tau, i
   const uint32_t* xl = xs + (chunk * (kWave * BPL) + lane) * 12;
 #pragma unroll
   for (int u = 0; u < BPL; ++u) {
-    const uint2 l = lut[g.c[u]];  // ids < 302 by construction (lvq_expand)
+    // ids < 302 by construction (lvq_expand); bit 15 is the gain bit (kGain)
+    const uint2 l = lut[M == kGain ? (g.c[u] & 0x7FFFu) : g.c[u]];
+    const float gam = M == kGain ? ((g.c[u] >> 15) ? ms.gain[1] : ms.gain[0]) : 1.f;
 #pragma unroll
     for (int wi = 0; wi < 3; ++wi) {
       uint32_t d[4];
@@ -269,11 +274,20 @@ __device__ __forceinline__ void decode_item(const MatSet& ms, int nb, int tau, i
 #pragma unroll
       for (int bb = 0; bb < B; ++bb) {
         const uint4 xq = *(const uint4*)(xl + bb * npair + u * (kWave * 12) + 4 * wi);
-        float& a = acc[bb][wi];
-        a = dot2(d[0], xq.x, a);
-        a = dot2(d[1], xq.y, a);
-        a = dot2(d[2], xq.z, a);
-        a = dot2(d[3], xq.w, a);
+        if (M == kGain) {
+          // the word's partial sum, times its block's gain
+          float pw = dot2(d[0], xq.x, 0.f);
+          pw = dot2(d[1], xq.y, pw);
+          pw = dot2(d[2], xq.z, pw);
+          pw = dot2(d[3], xq.w, pw);
+          acc[bb][wi] = __builtin_fmaf(pw, gam, acc[bb][wi]);
+        } else {
+          float& a = acc[bb][wi];
+          a = dot2(d[0], xq.x, a);
+          a = dot2(d[1], xq.y, a);
+          a = dot2(d[2], xq.z, a);
+          a = dot2(d[3], xq.w, a);
+        }
       }
     }
   }
@@ -312,11 +326,14 @@ __device__ __forceinline__ uint2 stage_lut(int c, uint64_t entry) {
 // Waves per SIMD the register allocation must leave room for: 8 (at most 64
 // VGPRs, two 1024-thread workgroups per CU) for the variants that fit there
 // without spilling, and whatever the allocation gives for the larger ones.
-constexpr int leech_min_waves(int B, int BPL) { return B + BPL <= 4 ? 8 : 1; }
+// (The shape-gain mode keeps a partial sum per word and goes without.)
+constexpr int leech_min_waves(int B, int BPL, int M) {
+  return M != kGain && B + BPL <= 4 ? 8 : 1;
+}
 
 template <int B, int BPL, int M>
 __global__ void __launch_bounds__(kMaxWgThreads)
-__attribute__((amdgpu_waves_per_eu(leech_min_waves(B, BPL))))
+__attribute__((amdgpu_waves_per_eu(leech_min_waves(B, BPL, M))))
 leech_gemv_kernel(MatSet ms, int rows, int nb, int tau, int cols, int nchunks, int kpad,
                   const uint16_t* __restrict__ x) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
@@ -520,11 +537,18 @@ int launch_leech_mode(const MatSet& ms, int rows, int cols, const uint16_t* x, h
   return launch_status();
 }
 
+// the shape-gain mode's extra partial sums do not fit 4 blocks per lane at
+// batch 2 (launch_leech never asks for it)
+constexpr bool gain_bpl_ok(int B, int BPL) { return !(B >= 2 && BPL >= 4); }
+
 template <int B, int BPL>
 int launch_leech_bpl(const MatSet& ms, int mode, int rows, int cols, const uint16_t* x,
                      hipStream_t st) {
   if (mode == kFused) return launch_leech_mode<B, BPL, kFused>(ms, rows, cols, x, st);
   if (mode == kNoWeights) return launch_leech_mode<B, BPL, kNoWeights>(ms, rows, cols, x, st);
+  if constexpr (gain_bpl_ok(B, BPL)) {
+    if (mode == kGain) return launch_leech_mode<B, BPL, kGain>(ms, rows, cols, x, st);
+  }
   return launch_leech_mode<B, BPL, kSingle>(ms, rows, cols, x, st);
 }
 
@@ -551,7 +575,7 @@ int launch_leech(const MatSet& ms, int n, int mode, int rows, int cols, const ui
     }
     return LVQ_OK;
   }
-  const int bpl = choose_bpl(nb, max_bpl(B), rows, device_cus());
+  const int bpl = choose_bpl(nb, mode == kGain && B >= 2 ? 3 : max_bpl(B), rows, device_cus());
   if constexpr (max_bpl(B) >= 4) {
     if (bpl == 4) return launch_leech_bpl<B, 4>(ms, mode, rows, cols, x, st);
   }
@@ -573,7 +597,7 @@ int launch_set(const MatSet& ms, int n, int mode, int rows, int cols, const uint
 }
 
 int single_gemv(const void* blob, int rows, int cols, const uint16_t* x, float* y, int batch,
-                void* stream, int mode) {
+                void* stream, int mode, float gain0 = 1.f, float gain1 = 1.f) {
   if (rows < 0 || cols < 0) return LVQ_E_SHAPE;
   int e = check_batch(batch);
   if (e) return e;
@@ -588,6 +612,8 @@ int single_gemv(const void* blob, int rows, int cols, const uint16_t* x, float* 
   ms.y[0] = y;
   ms.start[0] = 0;
   for (int i = 1; i <= kMaxFused; ++i) ms.start[i] = rows;
+  ms.gain[0] = gain0;
+  ms.gain[1] = gain1;
   return launch_set(ms, 1, mode, rows, cols, x, batch, st);
 }
 
@@ -598,6 +624,11 @@ using namespace lvq;
 extern "C" int lvq_gemv(const void* blob, int rows, int cols, const uint16_t* x, float* y,
                         int batch, void* stream) {
   return single_gemv(blob, rows, cols, x, y, batch, stream, kSingle);
+}
+
+extern "C" int lvq_gemv_gain(const void* blob, int rows, int cols, float gain0, float gain1,
+                             const uint16_t* x, float* y, int batch, void* stream) {
+  return single_gemv(blob, rows, cols, x, y, batch, stream, kGain, gain0, gain1);
 }
 
 extern "C" int lvq_gemv_noweights(const void* blob, int rows, int cols, const uint16_t* x,

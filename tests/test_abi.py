@@ -246,3 +246,64 @@ def test_rotate_validates_before_launch():
     assert r(A, None, None, 0, 1, A, 1, None) == lvq.LVQ_OK              # nothing to do
     # m > 1: y must not overlap x (the m workgroups of a row all read x)
     assert r(A, None, None, 3 * 1024, 3, A, 1, None) == lvq.LVQ_E_SHAPE
+
+
+def test_rank_matches_the_oracle():
+    from oracle import index as oi
+    rng = np.random.default_rng(48)
+    idx = [0, 1, oi.total() - 1, int(oi.block_offsets()[4096])]
+    idx += [int(v) for v in rng.integers(0, oi.total(), 400)]
+    pts = np.stack([oi.unrank(i) for i in idx])
+    got = lvq.rank(pts)
+    assert [int(v) for v in got] == idx
+    # shell-2 points from the classical construction: distinct ranks, and a
+    # sample agrees with the oracle's rank
+    pts2 = np.stack([synth.sample_class(c["key"], 300, rng)
+                     for c in leech.classes() if c["m"] == 2]).reshape(-1, 24)
+    r2 = lvq.rank(pts2)
+    for p, r in list(zip(pts2, r2))[::37]:
+        assert int(r) == oi.rank(p)
+    with pytest.raises(lvq.LvqError):
+        bad = pts[:1].copy()
+        bad[0, 0] += 2  # breaks the sum rule
+        lvq.rank(bad)
+    far = np.zeros((1, 24), dtype=np.int8)
+    far[0, :2] = [12, 12]  # a lattice point beyond shell 12... if it is one
+    if leech.is_leech(far[0]):
+        with pytest.raises(lvq.LvqError):
+            lvq.rank(far)
+
+
+def test_expand_gain_stores_the_gain_bit():
+    rows, nb, tau = 5, 7, 3
+    d = synth.leech_matrix(rows, 24 * nb + tau, 3)
+    g = np.random.default_rng(1).integers(0, 2, (rows, nb)).astype(np.uint8)
+    blob = lvq.expand_gain(d["coords"], g, d["scale"], d["tail"], rows, 24 * nb + tau)
+    plain = lvq.expand(d["coords"], d["scale"], d["tail"], rows, 24 * nb + tau)
+    sec = layout.sections(rows, 24 * nb + tau)
+    cls_g = blob[sec["cls"]: sec["cls"] + rows * nb * 2].view(np.uint16)
+    cls_p = plain[sec["cls"]: sec["cls"] + rows * nb * 2].view(np.uint16)
+    assert np.array_equal(cls_g & 0x7FFF, cls_p)
+    assert np.array_equal(cls_g >> 15, g.reshape(-1))
+    # everything else is the same blob
+    mask = np.ones(blob.size, dtype=bool)
+    mask[sec["cls"]: sec["cls"] + rows * nb * 2] = False
+    assert np.array_equal(blob[mask], plain[mask])
+    g[1, 2] = 2
+    with pytest.raises(lvq.LvqError):
+        lvq.expand_gain(d["coords"], g, d["scale"], d["tail"], rows, 24 * nb + tau)
+
+
+def test_unfold_and_gain_gemv_validate_before_launch():
+    lib = lvq.library()
+    A = 1 << 20
+    assert lib.lvq_unfold(None, 4, A, A, None) == lvq.LVQ_E_NULL
+    assert lib.lvq_unfold(A, 4, None, A, None) == lvq.LVQ_E_NULL
+    assert lib.lvq_unfold(A + 8, 4, A, A, None) == lvq.LVQ_E_ALIGN
+    assert lib.lvq_unfold(A, 0, A, A, None) == lvq.LVQ_OK
+    g = lib.lvq_gemv_gain
+    assert g(A, 4, 48, 1.0, 2.0, A, A, 0, None) == lvq.LVQ_E_BATCH
+    assert g(None, 4, 48, 1.0, 2.0, A, A, 1, None) == lvq.LVQ_E_NULL
+    assert g(A + 4, 4, 48, 1.0, 2.0, A, A, 1, None) == lvq.LVQ_E_ALIGN
+    assert g(A, 0, 48, 1.0, 2.0, A, A, 1, None) == lvq.LVQ_OK
+    assert lib.lvq_rank(None, 3, A) == lvq.LVQ_E_NULL
