@@ -28,6 +28,7 @@ LVQ_E_NOT_LEECH = -4
 LVQ_E_NORM = -5
 LVQ_E_BATCH = -6
 LVQ_E_HIP = -7
+LVQ_E_LAYOUT = -8
 
 
 class LvqError(RuntimeError):
@@ -58,6 +59,8 @@ def _load():
         "lvq_layout_bytes": (sz, [i, i]),
         "lvq_expand": (i, [vp, vp, vp, i, i, vp]),
         "lvq_expand_gain": (i, [vp, vp, vp, vp, i, i, vp]),
+        "lvq_layout_bytes_lp2": (sz, [i, i]),
+        "lvq_expand_lp2": (i, [vp, vp, vp, i, i, vp]),
         "lvq_rank": (i, [vp, sz, vp]),
         "lvq_unfold": (i, [vp, sz, vp, vp, vp]),
         "lvq_gemv_gain": (i, [vp, i, i, ctypes.c_float, ctypes.c_float, vp, vp, i, vp]),
@@ -80,7 +83,8 @@ def _load():
 
 _lib = _load()
 EXPORTED = ("lvq_strerror", "lvq_last_error_index", "lvq_class_table", "lvq_layout_bytes",
-            "lvq_expand", "lvq_expand_gain", "lvq_rank", "lvq_gemv", "lvq_gemv_gain",
+            "lvq_expand", "lvq_expand_gain", "lvq_layout_bytes_lp2", "lvq_expand_lp2",
+            "lvq_rank", "lvq_gemv", "lvq_gemv_gain",
             "lvq_unfold", "lvq_gemv_fused", "lvq_gemv_noweights", "lvq_decode",
             "bpdq_gemv", "trellis_gemv", "fp16_gemv", "lvq_rotate", "lvq_stream_read")
 
@@ -155,6 +159,28 @@ def expand(coords, scale, tail, rows: int, cols: int) -> np.ndarray:
     blob = np.empty(n, dtype=np.uint8)
     code = _lib.lvq_expand(_ptr(coords), _ptr(scale), _ptr(tail), int(rows), int(cols),
                            blob.ctypes.data)
+    if code != LVQ_OK:
+        r, b = ctypes.c_int(), ctypes.c_int()
+        _lib.lvq_last_error_index(ctypes.byref(r), ctypes.byref(b))
+        _check(code, (r.value, b.value))
+    return blob
+
+
+def layout_bytes_lp2(rows: int, cols: int) -> int:
+    return int(_lib.lvq_layout_bytes_lp2(int(rows), int(cols)))
+
+
+def expand_lp2(coords, scale, tail, rows: int, cols: int) -> np.ndarray:
+    """Host expansion into the LP2 layout (two rank planes, class in the record)."""
+    coords = np.ascontiguousarray(coords, dtype=np.int8)
+    scale = np.ascontiguousarray(scale, dtype=np.uint16)
+    tau = cols % 24
+    tail = None if tau == 0 else np.ascontiguousarray(tail, dtype=np.uint16)
+    if rows < 0 or cols < 0 or coords.size != rows * (cols // 24) * 24:
+        _check(LVQ_E_SHAPE)
+    blob = np.empty(_lib.lvq_layout_bytes_lp2(int(rows), int(cols)), dtype=np.uint8)
+    code = _lib.lvq_expand_lp2(_ptr(coords), _ptr(scale), _ptr(tail), int(rows), int(cols),
+                               blob.ctypes.data)
     if code != LVQ_OK:
         r, b = ctypes.c_int(), ctypes.c_int()
         _lib.lvq_last_error_index(ctypes.byref(r), ctypes.byref(b))

@@ -208,8 +208,9 @@ const ClassTable& table() {
 }  // namespace
 
 namespace {
+enum Format { kLp3, kLp2 };
 int expand_impl(const int8_t* coords, const uint8_t* gain_bits, const uint16_t* scale,
-                const uint16_t* tail, int rows, int cols, void* blob_out);
+                const uint16_t* tail, int rows, int cols, void* blob_out, Format fmt = kLp3);
 }  // namespace
 
 extern "C" {
@@ -224,6 +225,7 @@ const char* lvq_strerror(int code) {
     case LVQ_E_NORM: return "a lattice block lies beyond shell 12";
     case LVQ_E_BATCH: return "batch must be between 1 and 4";
     case LVQ_E_HIP: return "a HIP call or kernel launch failed";
+    case LVQ_E_LAYOUT: return "a block's class cannot be stored in the requested layout";
     default: return "unknown status";
   }
 }
@@ -253,6 +255,16 @@ int lvq_expand(const int8_t* coords, const uint16_t* scale, const uint16_t* tail
   return expand_impl(coords, nullptr, scale, tail, rows, cols, blob_out);
 }
 
+size_t lvq_layout_bytes_lp2(int rows, int cols) {
+  if (rows < 0 || cols < 0) return 0;
+  return lvq::lp2_sections((size_t)rows, (size_t)cols).total;
+}
+
+int lvq_expand_lp2(const int8_t* coords, const uint16_t* scale, const uint16_t* tail, int rows,
+                   int cols, void* blob_out) {
+  return expand_impl(coords, nullptr, scale, tail, rows, cols, blob_out, kLp2);
+}
+
 int lvq_expand_gain(const int8_t* coords, const uint8_t* gain_bits, const uint16_t* scale,
                     const uint16_t* tail, int rows, int cols, void* blob_out) {
   if (rows > 0 && cols >= 24 && !gain_bits) return LVQ_E_NULL;
@@ -264,7 +276,7 @@ int lvq_expand_gain(const int8_t* coords, const uint8_t* gain_bits, const uint16
 namespace {
 
 int expand_impl(const int8_t* coords, const uint8_t* gain_bits, const uint16_t* scale,
-                const uint16_t* tail, int rows, int cols, void* blob_out) {
+                const uint16_t* tail, int rows, int cols, void* blob_out, Format fmt) {
   g_err_row = g_err_block = -1;
   if (rows < 0 || cols < 0) return LVQ_E_SHAPE;
   const size_t R = (size_t)rows, nb = (size_t)cols / 24, tau = (size_t)cols % 24;
@@ -272,7 +284,8 @@ int expand_impl(const int8_t* coords, const uint8_t* gain_bits, const uint16_t* 
     return LVQ_E_NULL;
   const ClassTable& T = table();
   const Golay& G = golay();
-  const lvq::Sections s = lvq::blob_sections(R, (size_t)cols);
+  const lvq::Sections s = fmt == kLp2 ? lvq::lp2_sections(R, (size_t)cols)
+                                      : lvq::blob_sections(R, (size_t)cols);
   uint8_t* out = (uint8_t*)blob_out;
   std::memset(out, 0, s.total);
   std::memcpy(out + s.table, T.entries.data(), LVQ_NUM_CLASSES * 8);
@@ -315,6 +328,23 @@ int expand_impl(const int8_t* coords, const uint8_t* gain_bits, const uint16_t* 
       }
       const ClassInfo& c = T.cls[id];
       uint32_t w[3] = {0, 0, 0};
+      if (fmt == kLp2) {
+        if (id >= lvq::kLp2MaxClass || c.nmags > 4) {
+          g_err_row = (int)r;
+          g_err_block = (int)k;
+          return LVQ_E_LAYOUT;
+        }
+        for (int j = 0; j < 24; ++j) {
+          const int v = x[j];
+          const int jj = j & 7, vv = jj >> 1, h = jj & 1;
+          const uint32_t rk = (uint32_t)c.slot_of_mag[v < 0 ? -v : v] - 1;  // 0..3
+          w[j >> 3] |= rk << (2 * vv + 16 * h);
+          if (v >= 0) w[j >> 3] |= 1u << (8 + 2 * vv + 16 * h);
+        }
+        w[0] |= lvq::lp2_class_bits((uint32_t)id);
+        std::memcpy(codes + (r * nb + k) * 3, w, 12);
+        continue;
+      }
       for (int j = 0; j < 24; ++j) {
         int v = x[j];
         const int jj = j & 7;

@@ -25,4 +25,32 @@ inline Sections blob_sections(size_t rows, size_t cols) {
   return s;
 }
 
+// The LP2 blob: the same table, 12-byte code records with the class id inside,
+// no class section (cls == codes, 0 bytes), scales and tails as above.
+inline Sections lp2_sections(size_t rows, size_t cols) {
+  const size_t nb = cols / 24, tau = cols % 24;
+  Sections s;
+  s.table = 0;
+  s.codes = s.table + align256((size_t)LVQ_NUM_CLASSES * 8);
+  s.cls = s.codes;
+  s.scale = s.codes + align256(rows * nb * 12);
+  s.tail = s.scale + align256(rows * 2);
+  s.total = s.tail + align256(rows * tau * 2);
+  return s;
+}
+
+// LP2 code word w of a block holds coordinates 8w..8w+7: coordinate 8w+2v+h
+// (view v = 0..3, half h = 0, 1) has its rank at bits 2v+16h .. 2v+16h+1 and
+// its non-negative flag at bit 8+2v+16h.  Word 0's odd bits 9..15 and 25..31
+// hold the class id: id bit 2i at bit 9+2i, id bit 2i+1 at bit 25+2i (i < 4).
+constexpr int kLp2MaxClass = 256;
+inline uint32_t lp2_class_bits(uint32_t id) {
+  uint32_t w = 0;
+  for (int i = 0; i < 4; ++i) {
+    w |= ((id >> (2 * i)) & 1u) << (9 + 2 * i);
+    w |= ((id >> (2 * i + 1)) & 1u) << (25 + 2 * i);
+  }
+  return w;
+}
+
 }  // namespace lvq

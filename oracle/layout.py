@@ -160,3 +160,69 @@ def unpack_blob(blob, rows: int, cols: int) -> dict:
                 rp[p] |= ((rank >> p) & 1) << j
     return {"table": table, "cls": cls, "sign": sign, "r0": rp[0], "r1": rp[1],
             "r2": rp[2], "scale": scale, "tail": tail, "bad_slot": bad}
+
+
+# --------------------------------------------------------------------------
+# LP2: two rank planes, the class inside the code record
+# --------------------------------------------------------------------------
+#
+# Physical LP2 blob (the expander's packing for blocks whose class has at most
+# four distinct magnitudes and an id below 256, which covers shells m <= 8).
+# The paper reports smaller in-VRAM layouts than its served record (section 1,
+# contribution C2: layouts of 5.51, 4.80, 4.34 and 3.59 bits per weight); the
+# bit layout below is this library's:
+#   table  u64 [302]        as LP3
+#   codes  u32 [R][nb][3]   12 bytes per block, no class section
+#   scale  fp16 [R], tail fp16 [R][tau]
+# In word w, coordinate j = 8w + 2v + h (v = 0..3, h = 0, 1):
+#   bits 2v+16h .. 2v+16h+1   rank (0..3)
+#   bit 8+2v+16h              1 if x_j >= 0
+# Word 0, odd bits: class id bit 2i at bit 9+2i, bit 2i+1 at bit 25+2i (i<4).
+
+def sections_lp2(rows: int, cols: int) -> dict:
+    nb, tau = cols // 24, cols % 24
+    off = {}
+    pos = 0
+    for name, size in (("table", TABLE_ENTRIES * 8), ("codes", rows * nb * 12),
+                       ("scale", rows * 2), ("tail", rows * tau * 2)):
+        off[name] = pos
+        pos += _align(size)
+    off["total"] = pos
+    return off
+
+
+def lp2_bytes(rows: int, cols: int) -> int:
+    """LP2 weight bytes: 12 per block, 2 per row, 2 per tail column."""
+    nb, tau = cols // 24, cols % 24
+    return rows * (12 * nb + 2 + 2 * tau)
+
+
+def unpack_lp2(blob, rows: int, cols: int) -> dict:
+    """Coordinates int8 [R][nb][24], class ids, scales and tails from an LP2
+    blob, read from the byte layout and the oracle's class table alone."""
+    buf = np.frombuffer(bytes(blob), dtype=np.uint8)
+    off = sections_lp2(rows, cols)
+    assert buf.size == off["total"], (buf.size, off["total"])
+    nb, tau = cols // 24, cols % 24
+    words = buf[off["codes"]: off["codes"] + rows * nb * 12].view("<u4").reshape(rows * nb, 3)
+    words = words.astype(np.int64)
+    cls = np.zeros(rows * nb, dtype=np.int64)
+    for i in range(4):
+        cls |= ((words[:, 0] >> (9 + 2 * i)) & 1) << (2 * i)
+        cls |= ((words[:, 0] >> (25 + 2 * i)) & 1) << (2 * i + 1)
+    classes = leech.classes()
+    mags = np.zeros((len(classes), 4), dtype=np.int64)
+    for cid, c in enumerate(classes):
+        dm = sorted(set(c["key"]))
+        mags[cid, : len(dm)] = dm[:4]
+    coords = np.zeros((rows * nb, 24), dtype=np.int64)
+    for j in range(24):
+        w, jj = divmod(j, 8)
+        v, h = jj // 2, jj % 2
+        rank = (words[:, w] >> (2 * v + 16 * h)) & 3
+        nonneg = (words[:, w] >> (8 + 2 * v + 16 * h)) & 1
+        mag = mags[cls, rank]
+        coords[:, j] = np.where(nonneg == 1, mag, -mag)
+    return {"coords": coords.astype(np.int8).reshape(rows, nb, 24), "cls": cls.reshape(rows, nb),
+            "scale": buf[off["scale"]: off["scale"] + rows * 2].view("<u2").copy(),
+            "tail": buf[off["tail"]: off["tail"] + rows * tau * 2].view("<u2").reshape(rows, tau).copy()}

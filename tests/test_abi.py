@@ -307,3 +307,35 @@ def test_unfold_and_gain_gemv_validate_before_launch():
     assert g(A + 4, 4, 48, 1.0, 2.0, A, A, 1, None) == lvq.LVQ_E_ALIGN
     assert g(A, 0, 48, 1.0, 2.0, A, A, 1, None) == lvq.LVQ_OK
     assert lib.lvq_rank(None, 3, A) == lvq.LVQ_E_NULL
+
+
+@pytest.mark.parametrize("rows,nb,tau,cfg", [(7, 11, 5, 3), (33, 170, 0, 4), (4, 3, 23, 1)])
+def test_expand_lp2_round_trips_through_the_oracle_unpacker(rows, nb, tau, cfg):
+    cols = 24 * nb + tau
+    d = synth.leech_matrix(rows, cols, cfg, key=(rows, nb, tau))
+    blob = lvq.expand_lp2(d["coords"], d["scale"], d["tail"], rows, cols)
+    assert blob.size == lvq.layout_bytes_lp2(rows, cols) == layout.sections_lp2(rows, cols)["total"]
+    u = layout.unpack_lp2(blob, rows, cols)
+    assert np.array_equal(u["coords"], d["coords"])
+    assert np.array_equal(u["scale"], d["scale"]) and np.array_equal(u["tail"], d["tail"])
+    assert np.array_equal(u["cls"], np.vectorize(lambda i: i)(
+        [[leech.class_of(b) for b in row] for row in d["coords"]]))
+
+
+def test_expand_lp2_every_small_class_and_the_refusals():
+    rng = np.random.default_rng(9)
+    ok = [c for c in leech.classes() if c["id"] < 256 and len(set(c["key"])) <= 4]
+    pts = np.stack([synth.sample_class(c["key"], 1, rng)[0] if c["id"] else np.zeros(24, np.int8)
+                    for c in ok])
+    rows = len(ok)
+    scale = synth.fp16_bits(np.ones(rows))
+    blob = lvq.expand_lp2(pts.reshape(rows, 1, 24), scale, None, rows, 24)
+    assert np.array_equal(layout.unpack_lp2(blob, rows, 24)["coords"].reshape(rows, 24), pts)
+    # a class with five distinct magnitudes is refused, and reported
+    five = next(c for c in leech.classes() if len(set(c["key"])) == 5)
+    x = np.zeros((2, 2, 24), dtype=np.int8)
+    x[1, 1] = synth.sample_class(five["key"], 1, rng)[0]
+    with pytest.raises(lvq.LvqError) as e:
+        lvq.expand_lp2(x, synth.fp16_bits(np.ones(2)), None, 2, 48)
+    assert e.value.code == lvq.LVQ_E_LAYOUT and e.value.index == (1, 1)
+    assert lvq.strerror(lvq.LVQ_E_LAYOUT).startswith("a block's class")
