@@ -194,6 +194,13 @@ def leech_bytes(rows, cols):
     return rows * (14 * nb + 2 + 2 * tau)
 
 
+def lp2_bytes(rows, cols):
+    """LP2: 12 B per 24-weight block (ranks, signs and class), 2 B per row
+    for the scale, 2 B per unquantized tail column."""
+    nb, tau = cols // 24, cols % 24
+    return rows * (12 * nb + 2 + 2 * tau)
+
+
 def bpdq_bytes(rows, cols):
     return (cols // 16) * rows * 4 + (cols // 256) * 3 * rows * 2
 
@@ -382,6 +389,43 @@ class Bench:
                "bytes_in": 8 * nblocks, "bytes_out": 25 * nblocks, "trials": self.args.trials}
         log("unfold   %d blocks: %.1f us (%.3f G blocks/s)" % (nblocks, us, rec["gblocks_per_s"]))
         return rec
+
+    def leech_lp2(self, cfg, rows, cols, batch, d=None):
+        """The LP2 layout (two rank planes, class in the record) at one shape."""
+        import synth
+        torch, lvq = self.torch, self.lvq
+        if d is None:
+            d = synth.leech_matrix(rows, cols, cfg)
+        blob = lvq.expand_lp2(d["coords"], d["scale"], d["tail"], rows, cols)
+        x = synth.activations(cols, batch, cfg, rows=rows)
+        n = copies_for(blob.size)
+        bufs = dev_copies(torch, blob, n)
+        xd = to_dev(torch, x)
+        yd = torch.empty((batch, rows), dtype=torch.float32, device="cuda")
+        tm = self.time(lambda i: lvq.gemv_lp2(bufs[i % n], rows, cols, xd, yd, batch))
+        del bufs
+        torch.cuda.empty_cache()
+        return self.record("leech_lp2", cfg, rows, cols, batch, lp2_bytes(rows, cols), n, tm,
+                           blob_bytes=int(blob.size))
+
+    def leech_lp2x(self, cfg, rows, cols, batch, d=None):
+        """LP2 with the exception side channel (two launches) at one shape."""
+        import synth
+        torch, lvq = self.torch, self.lvq
+        if d is None:
+            d = synth.leech_matrix(rows, cols, cfg)
+        blob, n_exc = lvq.expand_lp2x(d["coords"], d["scale"], d["tail"], rows, cols)
+        x = synth.activations(cols, batch, cfg, rows=rows)
+        n = copies_for(blob.size)
+        bufs = dev_copies(torch, blob, n)
+        xd = to_dev(torch, x)
+        yd = torch.empty((batch, rows), dtype=torch.float32, device="cuda")
+        tm = self.time(lambda i: lvq.gemv_lp2x(bufs[i % n], rows, cols, n_exc, xd, yd, batch))
+        del bufs
+        torch.cuda.empty_cache()
+        nbytes = lp2_bytes(rows, cols) + 16 * n_exc + 4 * (rows + 1)
+        return self.record("leech_lp2x", cfg, rows, cols, batch, nbytes, n, tm,
+                           side_channel_blocks=int(n_exc), blob_bytes=int(blob.size))
 
     def leech_gain(self, rows, cols, batch):
         """The shape-gain GEMV at one shape (random gain bits, two gain levels)."""
@@ -708,6 +752,13 @@ def main():
             records.append(B.rotate(n, m, 1))
         records.append(B.rotate(12288, 3, 4))
         records.append(B.leech_gain(ROWS, COLS, 1))
+        records.append(B.leech_lp2(4, ROWS, COLS, 1, d=d))
+        records.append(B.leech_lp2(4, ROWS, COLS, 4, d=d))
+        for rows in (4096, 12288):
+            records.append(B.leech_lp2(3, rows, 4096, 1))
+        d6 = __import__("synth").leech_matrix(ROWS, COLS, 6)
+        records.append(B.leech(6, ROWS, COLS, 1, d=d6))
+        records.append(B.leech_lp2x(6, ROWS, COLS, 1, d=d6))
         records.append(B.unfold(ROWS * (COLS // 24)))
         fp16_by_shape = {(r["R"], r["K"]): r["gbps"] for r in records if r["arm"] == "fp16"}
         for r in records:

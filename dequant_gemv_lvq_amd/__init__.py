@@ -61,6 +61,11 @@ def _load():
         "lvq_expand_gain": (i, [vp, vp, vp, vp, i, i, vp]),
         "lvq_layout_bytes_lp2": (sz, [i, i]),
         "lvq_expand_lp2": (i, [vp, vp, vp, i, i, vp]),
+        "lvq_gemv_lp2": (i, [vp, i, i, vp, vp, i, vp]),
+        "lvq_lp2x_exceptions": (i, [vp, i, i, vp]),
+        "lvq_layout_bytes_lp2x": (sz, [i, i, sz]),
+        "lvq_expand_lp2x": (i, [vp, vp, vp, i, i, sz, vp]),
+        "lvq_gemv_lp2x": (i, [vp, i, i, sz, vp, vp, i, vp]),
         "lvq_rank": (i, [vp, sz, vp]),
         "lvq_unfold": (i, [vp, sz, vp, vp, vp]),
         "lvq_gemv_gain": (i, [vp, i, i, ctypes.c_float, ctypes.c_float, vp, vp, i, vp]),
@@ -84,6 +89,8 @@ def _load():
 _lib = _load()
 EXPORTED = ("lvq_strerror", "lvq_last_error_index", "lvq_class_table", "lvq_layout_bytes",
             "lvq_expand", "lvq_expand_gain", "lvq_layout_bytes_lp2", "lvq_expand_lp2",
+            "lvq_gemv_lp2", "lvq_lp2x_exceptions", "lvq_layout_bytes_lp2x", "lvq_expand_lp2x",
+            "lvq_gemv_lp2x",
             "lvq_rank", "lvq_gemv", "lvq_gemv_gain",
             "lvq_unfold", "lvq_gemv_fused", "lvq_gemv_noweights", "lvq_decode",
             "bpdq_gemv", "trellis_gemv", "fp16_gemv", "lvq_rotate", "lvq_stream_read")
@@ -188,6 +195,27 @@ def expand_lp2(coords, scale, tail, rows: int, cols: int) -> np.ndarray:
     return blob
 
 
+def expand_lp2x(coords, scale, tail, rows: int, cols: int) -> tuple:
+    """Host expansion into LP2X; returns (blob, number of side-channel blocks)."""
+    coords = np.ascontiguousarray(coords, dtype=np.int8)
+    scale = np.ascontiguousarray(scale, dtype=np.uint16)
+    tau = cols % 24
+    tail = None if tau == 0 else np.ascontiguousarray(tail, dtype=np.uint16)
+    if rows < 0 or cols < 0 or coords.size != rows * (cols // 24) * 24:
+        _check(LVQ_E_SHAPE)
+    n = ctypes.c_size_t()
+    code = _lib.lvq_lp2x_exceptions(_ptr(coords), int(rows), int(cols), ctypes.byref(n))
+    if code == LVQ_OK:
+        blob = np.empty(_lib.lvq_layout_bytes_lp2x(int(rows), int(cols), n.value), dtype=np.uint8)
+        code = _lib.lvq_expand_lp2x(_ptr(coords), _ptr(scale), _ptr(tail), int(rows), int(cols),
+                                    n.value, blob.ctypes.data)
+    if code != LVQ_OK:
+        r, b = ctypes.c_int(), ctypes.c_int()
+        _lib.lvq_last_error_index(ctypes.byref(r), ctypes.byref(b))
+        _check(code, (r.value, b.value))
+    return blob, n.value
+
+
 def expand_gain(coords, gain_bits, scale, tail, rows: int, cols: int) -> np.ndarray:
     """lvq_expand with a shape-gain bit per block (uint8 [rows][cols//24])."""
     coords = np.ascontiguousarray(coords, dtype=np.int8)
@@ -246,6 +274,17 @@ def gemv_noweights(blob, rows: int, cols: int, x, y, batch: int = 1, stream=None
     bytes (y = 0); blob only supplies the class table."""
     _check(_lib.lvq_gemv_noweights(_ptr(blob), int(rows), int(cols), _ptr(x), _ptr(y),
                                    int(batch), _stream(stream)))
+
+
+def gemv_lp2(blob, rows: int, cols: int, x, y, batch: int = 1, stream=None):
+    _check(_lib.lvq_gemv_lp2(_ptr(blob), int(rows), int(cols), _ptr(x), _ptr(y), int(batch),
+                             _stream(stream)))
+
+
+def gemv_lp2x(blob, rows: int, cols: int, n_exceptions: int, x, y, batch: int = 1,
+              stream=None):
+    _check(_lib.lvq_gemv_lp2x(_ptr(blob), int(rows), int(cols), int(n_exceptions), _ptr(x),
+                              _ptr(y), int(batch), _stream(stream)))
 
 
 def gemv_gain(blob, rows: int, cols: int, gain0: float, gain1: float, x, y, batch: int = 1,

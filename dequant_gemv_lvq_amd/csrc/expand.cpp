@@ -208,9 +208,12 @@ const ClassTable& table() {
 }  // namespace
 
 namespace {
-enum Format { kLp3, kLp2 };
+enum Format { kLp3, kLp2, kLp2x };
 int expand_impl(const int8_t* coords, const uint8_t* gain_bits, const uint16_t* scale,
-                const uint16_t* tail, int rows, int cols, void* blob_out, Format fmt = kLp3);
+                const uint16_t* tail, int rows, int cols, void* blob_out, Format fmt = kLp3,
+                size_t n_exc = 0);
+int classify(const int8_t* x, int* id_out);
+bool lp2_eligible(int id);
 }  // namespace
 
 extern "C" {
@@ -265,6 +268,36 @@ int lvq_expand_lp2(const int8_t* coords, const uint16_t* scale, const uint16_t* 
   return expand_impl(coords, nullptr, scale, tail, rows, cols, blob_out, kLp2);
 }
 
+int lvq_lp2x_exceptions(const int8_t* coords, int rows, int cols, size_t* n_exceptions) {
+  g_err_row = g_err_block = -1;
+  if (rows < 0 || cols < 0) return LVQ_E_SHAPE;
+  if (!n_exceptions || (rows && cols >= 24 && !coords)) return LVQ_E_NULL;
+  const size_t nb = (size_t)cols / 24;
+  size_t n = 0;
+  for (size_t b = 0; b < (size_t)rows * nb; ++b) {
+    int id = 0;
+    const int err = classify(coords + b * 24, &id);
+    if (err) {
+      g_err_row = (int)(b / nb);
+      g_err_block = (int)(b % nb);
+      return err;
+    }
+    n += lp2_eligible(id) ? 0 : 1;
+  }
+  *n_exceptions = n;
+  return LVQ_OK;
+}
+
+size_t lvq_layout_bytes_lp2x(int rows, int cols, size_t n_exceptions) {
+  if (rows < 0 || cols < 0) return 0;
+  return lvq::lp2x_sections((size_t)rows, (size_t)cols, n_exceptions).total;
+}
+
+int lvq_expand_lp2x(const int8_t* coords, const uint16_t* scale, const uint16_t* tail, int rows,
+                    int cols, size_t n_exceptions, void* blob_out) {
+  return expand_impl(coords, nullptr, scale, tail, rows, cols, blob_out, kLp2x, n_exceptions);
+}
+
 int lvq_expand_gain(const int8_t* coords, const uint8_t* gain_bits, const uint16_t* scale,
                     const uint16_t* tail, int rows, int cols, void* blob_out) {
   if (rows > 0 && cols >= 24 && !gain_bits) return LVQ_E_NULL;
@@ -275,84 +308,112 @@ int lvq_expand_gain(const int8_t* coords, const uint8_t* gain_bits, const uint16
 
 namespace {
 
+// Membership, norm and class of one block: LVQ_OK and the class id, or the
+// error code.
+int classify(const int8_t* x, int* id_out) {
+  const ClassTable& T = table();
+  const Golay& G = golay();
+  const int par = x[0] & 1;
+  bool same = true;
+  uint32_t mask = 0;
+  int sum = 0, norm = 0;
+  for (int j = 0; j < 24; ++j) {
+    const int v = x[j];
+    same &= (v & 1) == par;
+    const int r4 = v & 3;  // two's complement: v mod 4
+    if (r4 == (par ? 3 : 2)) mask |= 1u << j;
+    sum += v;
+    norm += v * v;
+  }
+  if (!(same && G.contains(mask) && (sum & 7) == (par ? 4 : 0))) return LVQ_E_NOT_LEECH;
+  if (norm > 16 * kMaxShell) return LVQ_E_NORM;
+  int counts[kMaxMag + 1] = {0};
+  for (int j = 0; j < 24; ++j) counts[x[j] < 0 ? -x[j] : x[j]]++;
+  const int id = T.lookup(count_key_of(counts));
+  if (id < 0) return LVQ_E_NOT_LEECH;  // a lattice point of shell <= 12 always has a class
+  *id_out = id;
+  return LVQ_OK;
+}
+
+bool lp2_eligible(int id) { return id < lvq::kLp2MaxClass && table().cls[id].nmags <= 4; }
+
+void pack_lp3(const int8_t* x, const ClassInfo& c, uint32_t w[3]) {
+  w[0] = w[1] = w[2] = 0;
+  for (int j = 0; j < 24; ++j) {
+    const int v = x[j];
+    const int jj = j & 7;
+    const int n = (jj >> 1) + 4 * (jj & 1);  // slot of coordinate j
+    const uint32_t slot = c.slot_of_mag[v < 0 ? -v : v];
+    w[j >> 3] |= slot << (4 * n);
+    if (v >= 0) w[j >> 3] |= 1u << ((4 * n + 11) & 31);
+  }
+}
+
+void pack_lp2(const int8_t* x, const ClassInfo& c, int id, uint32_t w[3]) {
+  w[0] = w[1] = w[2] = 0;
+  for (int j = 0; j < 24; ++j) {
+    const int v = x[j];
+    const int jj = j & 7, vv = jj >> 1, h = jj & 1;
+    const uint32_t rk = (uint32_t)c.slot_of_mag[v < 0 ? -v : v] - 1;  // 0..3
+    w[j >> 3] |= rk << (2 * vv + 16 * h);
+    if (v >= 0) w[j >> 3] |= 1u << (8 + 2 * vv + 16 * h);
+  }
+  w[0] |= lvq::lp2_class_bits((uint32_t)id);
+}
+
 int expand_impl(const int8_t* coords, const uint8_t* gain_bits, const uint16_t* scale,
-                const uint16_t* tail, int rows, int cols, void* blob_out, Format fmt) {
+                const uint16_t* tail, int rows, int cols, void* blob_out, Format fmt,
+                size_t n_exc) {
   g_err_row = g_err_block = -1;
   if (rows < 0 || cols < 0) return LVQ_E_SHAPE;
   const size_t R = (size_t)rows, nb = (size_t)cols / 24, tau = (size_t)cols % 24;
   if (!blob_out || (R && !scale) || (R && nb && !coords) || (R && tau && !tail))
     return LVQ_E_NULL;
   const ClassTable& T = table();
-  const Golay& G = golay();
-  const lvq::Sections s = fmt == kLp2 ? lvq::lp2_sections(R, (size_t)cols)
-                                      : lvq::blob_sections(R, (size_t)cols);
+  const lvq::Sections s = fmt == kLp3 ? lvq::blob_sections(R, (size_t)cols)
+                                      : lvq::lp2_sections(R, (size_t)cols);
+  const lvq::Lp2xSections sx = lvq::lp2x_sections(R, (size_t)cols, n_exc);
   uint8_t* out = (uint8_t*)blob_out;
-  std::memset(out, 0, s.total);
+  std::memset(out, 0, fmt == kLp2x ? sx.total : s.total);
   std::memcpy(out + s.table, T.entries.data(), LVQ_NUM_CLASSES * 8);
   uint32_t* codes = (uint32_t*)(out + s.codes);
   uint16_t* cls = (uint16_t*)(out + s.cls);
+  uint32_t* exc_off = (uint32_t*)(out + sx.exc_off);
+  uint32_t* exc = (uint32_t*)(out + sx.exc);
+  size_t e = 0;
   for (size_t r = 0; r < R; ++r) {
+    if (fmt == kLp2x) exc_off[r] = (uint32_t)e;
     for (size_t k = 0; k < nb; ++k) {
       const int8_t* x = coords + (r * nb + k) * 24;
-      // membership: one parity, Golay pattern of residues, sum mod 8
-      int par = x[0] & 1;
-      bool same = true;
-      uint32_t mask = 0;
-      int sum = 0, norm = 0;
-      for (int j = 0; j < 24; ++j) {
-        int v = x[j];
-        same &= (v & 1) == par;
-        int r4 = v & 3;  // two's complement: v mod 4
-        if (r4 == (par ? 3 : 2)) mask |= 1u << j;
-        sum += v;
-        norm += v * v;
-      }
-      bool ok = same && G.contains(mask) && (sum & 7) == (par ? 4 : 0);
-      if (!ok) {
+      int id = 0;
+      const int err = classify(x, &id);
+      if (err) {
         g_err_row = (int)r;
         g_err_block = (int)k;
-        return LVQ_E_NOT_LEECH;
-      }
-      if (norm > 16 * kMaxShell) {
-        g_err_row = (int)r;
-        g_err_block = (int)k;
-        return LVQ_E_NORM;
-      }
-      int counts[kMaxMag + 1] = {0};
-      for (int j = 0; j < 24; ++j) counts[x[j] < 0 ? -x[j] : x[j]]++;
-      int id = T.lookup(count_key_of(counts));
-      if (id < 0) {  // a lattice point of shell <= 12 always has a class
-        g_err_row = (int)r;
-        g_err_block = (int)k;
-        return LVQ_E_NOT_LEECH;
+        return err;
       }
       const ClassInfo& c = T.cls[id];
-      uint32_t w[3] = {0, 0, 0};
-      if (fmt == kLp2) {
-        if (id >= lvq::kLp2MaxClass || c.nmags > 4) {
+      uint32_t w[3];
+      if (fmt != kLp3) {
+        if (lp2_eligible(id)) {
+          pack_lp2(x, c, id, w);
+          std::memcpy(codes + (r * nb + k) * 3, w, 12);
+        } else if (fmt == kLp2x) {
+          // the side channel: block index, class, and the LP3 record; the
+          // main record stays zero (the origin)
+          if (e >= n_exc) return LVQ_E_SHAPE;
+          pack_lp3(x, c, w);
+          exc[4 * e] = (uint32_t)k | ((uint32_t)id << 16);
+          std::memcpy(exc + 4 * e + 1, w, 12);
+          ++e;
+        } else {
           g_err_row = (int)r;
           g_err_block = (int)k;
           return LVQ_E_LAYOUT;
         }
-        for (int j = 0; j < 24; ++j) {
-          const int v = x[j];
-          const int jj = j & 7, vv = jj >> 1, h = jj & 1;
-          const uint32_t rk = (uint32_t)c.slot_of_mag[v < 0 ? -v : v] - 1;  // 0..3
-          w[j >> 3] |= rk << (2 * vv + 16 * h);
-          if (v >= 0) w[j >> 3] |= 1u << (8 + 2 * vv + 16 * h);
-        }
-        w[0] |= lvq::lp2_class_bits((uint32_t)id);
-        std::memcpy(codes + (r * nb + k) * 3, w, 12);
         continue;
       }
-      for (int j = 0; j < 24; ++j) {
-        int v = x[j];
-        const int jj = j & 7;
-        const int n = (jj >> 1) + 4 * (jj & 1);  // slot of coordinate j
-        uint32_t slot = c.slot_of_mag[v < 0 ? -v : v];
-        w[j >> 3] |= slot << (4 * n);
-        if (v >= 0) w[j >> 3] |= 1u << ((4 * n + 11) & 31);
-      }
+      pack_lp3(x, c, w);
       std::memcpy(codes + (r * nb + k) * 3, w, 12);
       uint16_t g = 0;
       if (gain_bits) {
@@ -365,6 +426,10 @@ int expand_impl(const int8_t* coords, const uint8_t* gain_bits, const uint16_t* 
       }
       cls[r * nb + k] = (uint16_t)(id | g);
     }
+  }
+  if (fmt == kLp2x) {
+    if (e != n_exc) return LVQ_E_SHAPE;
+    exc_off[R] = (uint32_t)e;
   }
   if (R) std::memcpy(out + s.scale, scale, R * 2);
   if (R && tau) std::memcpy(out + s.tail, tail, R * tau * 2);

@@ -39,6 +39,20 @@ inline Sections lp2_sections(size_t rows, size_t cols) {
   return s;
 }
 
+// LP2X: the LP2 blob followed by an exception side channel for the blocks LP2
+// cannot hold (their main record is zero): row offsets u32 [rows + 1] and
+// 16-byte entries {block index | class id << 16, the three LP3 code words}.
+struct Lp2xSections {
+  size_t exc_off, exc, total;
+};
+inline Lp2xSections lp2x_sections(size_t rows, size_t cols, size_t n_exc) {
+  Lp2xSections x;
+  x.exc_off = lp2_sections(rows, cols).total;
+  x.exc = x.exc_off + align256((rows + 1) * 4);
+  x.total = x.exc + align256(n_exc * 16);
+  return x;
+}
+
 // LP2 code word w of a block holds coordinates 8w..8w+7: coordinate 8w+2v+h
 // (view v = 0..3, half h = 0, 1) has its rank at bits 2v+16h .. 2v+16h+1 and
 // its non-negative flag at bit 8+2v+16h.  Word 0's odd bits 9..15 and 25..31

@@ -86,6 +86,18 @@ struct LeechView {
   const uint16_t* tail;
 };
 
+__host__ __device__ inline LeechView lp2_view(const void* blob, size_t rows, size_t cols) {
+  const Sections s = lp2_sections(rows, cols);
+  const uint8_t* b = (const uint8_t*)blob;
+  LeechView v;
+  v.table = (const uint64_t*)(b + s.table);
+  v.codes = (const uint32_t*)(b + s.codes);
+  v.cls = nullptr;
+  v.scale = (const uint16_t*)(b + s.scale);
+  v.tail = (const uint16_t*)(b + s.tail);
+  return v;
+}
+
 __host__ __device__ inline LeechView leech_view(const void* blob, size_t rows, size_t cols) {
   const Sections s = blob_sections(rows, cols);
   const uint8_t* b = (const uint8_t*)blob;
@@ -125,7 +137,8 @@ constexpr int kStream = 2;
 constexpr int kMaxFused = 4;
 // kGain: one matrix whose class ids carry a shape-gain bit in bit 15; the
 // block's weights are multiplied by gain[bit]
-constexpr int kSingle = 0, kFused = 1, kNoWeights = 2, kGain = 3;
+// kLp2: one matrix in the LP2 layout (two rank planes, class in the record)
+constexpr int kSingle = 0, kFused = 1, kNoWeights = 2, kGain = 3, kLp2 = 4;
 
 struct MatSet {
   LeechView v[kMaxFused];
@@ -185,6 +198,20 @@ struct ItemRegs {
   uint32_t scale;  // the row's fp16 scale
 };
 
+// LP2: bytes 0..3 the first four ascending magnitudes (rank selectors 0..3),
+// byte 4 = 0x80 (negative), byte 5 = 0x00 (non-negative)
+__device__ __forceinline__ uint2 stage_lut_lp2(uint64_t entry) {
+  return make_uint2((uint32_t)entry, 0x80u);
+}
+
+// LP2 view v of a code word: selector bytes [rank A, 4 + nonneg A, rank B,
+// 4 + nonneg B] in one AND-OR, then one byte permute
+__device__ __forceinline__ uint32_t lp2_pair(uint32_t word, int v, uint32_t lut_lo,
+                                             uint32_t lut_hi) {
+  const uint32_t w = v ? word >> (2 * v) : word;
+  return __builtin_amdgcn_perm(lut_hi, lut_lo, (w & 0x01030103u) | 0x04000400u);
+}
+
 // An item's loads come in two groups: its metadata (class ids, this lane's
 // tail value, the row scale: everything the table lookups and the epilogue
 // need) and its code words.  In the no-weights mode every load is issued
@@ -205,11 +232,13 @@ __device__ __forceinline__ void load_meta(const MatSet& ms, int nb, int tau, int
   const uint16_t* tail = pick<M>(ms, m, [](const MatSet& s, int i) { return s.v[i].tail; });
   const uint16_t* scale = pick<M>(ms, m, [](const MatSet& s, int i) { return s.v[i].scale; });
   const int k0 = chunk * (kWave * BPL);
-  const auto rc =
-      buffer_rsrc(cls + (size_t)r * nb + k0, weight_bytes<M>((uint32_t)(nb - k0) * 2));
+  if (M != kLp2) {  // LP2 keeps the class inside the code record
+    const auto rc =
+        buffer_rsrc(cls + (size_t)r * nb + k0, weight_bytes<M>((uint32_t)(nb - k0) * 2));
 #pragma unroll
-  for (int u = 0; u < BPL; ++u)
-    g.c[u] = __builtin_amdgcn_raw_buffer_load_b16(rc, (lane + u * kWave) * 2, 0, kStream);
+    for (int u = 0; u < BPL; ++u)
+      g.c[u] = __builtin_amdgcn_raw_buffer_load_b16(rc, (lane + u * kWave) * 2, 0, kStream);
+  }
   const auto rt = buffer_rsrc(tail + (size_t)r * tau, weight_bytes<M>((uint32_t)tau * 2));
   g.tail = __builtin_amdgcn_raw_buffer_load_b16(rt, lane * 2, 0, 0);
   // the row scale, read by every lane (one transaction); a vector load, so
@@ -263,14 +292,20 @@ __device__ __forceinline__ void decode_item(const MatSet& ms, int nb, int tau, i
   const uint32_t* xl = xs + (chunk * (kWave * BPL) + lane) * 12;
 #pragma unroll
   for (int u = 0; u < BPL; ++u) {
-    // ids < 302 by construction (lvq_expand); bit 15 is the gain bit (kGain)
-    const uint2 l = lut[M == kGain ? (g.c[u] & 0x7FFFu) : g.c[u]];
+    // ids < 302 by construction (lvq_expand); bit 15 is the gain bit (kGain);
+    // LP2: the id sits in the odd bits 9..15 and 25..31 of word 0
+    const uint32_t w0 = g.w[u][0];
+    const uint32_t cid = M == kLp2 ? (((w0 >> 9) & 0x55u) | ((w0 >> 24) & 0xAAu))
+                       : M == kGain ? (g.c[u] & 0x7FFFu) : g.c[u];
+    const uint2 l = lut[cid];
     const float gam = M == kGain ? ((g.c[u] >> 15) ? ms.gain[1] : ms.gain[0]) : 1.f;
 #pragma unroll
     for (int wi = 0; wi < 3; ++wi) {
       uint32_t d[4];
 #pragma unroll
-      for (int vi = 0; vi < 4; ++vi) d[vi] = leech_pair(g.w[u][wi], vi, l.x, l.y);
+      for (int vi = 0; vi < 4; ++vi)
+        d[vi] = M == kLp2 ? lp2_pair(g.w[u][wi], vi, l.x, l.y)
+                          : leech_pair(g.w[u][wi], vi, l.x, l.y);
 #pragma unroll
       for (int bb = 0; bb < B; ++bb) {
         const uint4 xq = *(const uint4*)(xl + bb * npair + u * (kWave * 12) + 4 * wi);
@@ -326,9 +361,10 @@ __device__ __forceinline__ uint2 stage_lut(int c, uint64_t entry) {
 // Waves per SIMD the register allocation must leave room for: 8 (at most 64
 // VGPRs, two 1024-thread workgroups per CU) for the variants that fit there
 // without spilling, and whatever the allocation gives for the larger ones.
-// (The shape-gain mode keeps a partial sum per word and goes without.)
+// (The shape-gain mode keeps a partial sum per word and goes without, and so
+// does LP2 above batch 1, whose class extraction needs the registers.)
 constexpr int leech_min_waves(int B, int BPL, int M) {
-  return M != kGain && B + BPL <= 4 ? 8 : 1;
+  return M != kGain && !(M == kLp2 && B > 1) && B + BPL <= 4 ? 8 : 1;
 }
 
 template <int B, int BPL, int M>
@@ -388,7 +424,10 @@ leech_gemv_kernel(MatSet ms, int rows, int nb, int tau, int cols, int nchunks, i
   load_item<BPL, M>(ms, nb, tau, rb, cb, lane, ib);
   asm volatile("" ::: "memory");
   // 3. the class table into LDS; the barrier also waits for x
-  for (int c = tid; c < LVQ_NUM_CLASSES; c += nthr) lut[c] = stage_lut(c, c == tid ? te : table[c]);
+  for (int c = tid; c < LVQ_NUM_CLASSES; c += nthr) {
+    const uint64_t e = c == tid ? te : table[c];
+    lut[c] = M == kLp2 ? stage_lut_lp2(e) : stage_lut(c, e);
+  }
   __syncthreads();
 
   float acc[B][3];
@@ -423,6 +462,51 @@ leech_gemv_kernel(MatSet ms, int rows, int nb, int tau, int cols, int nchunks, i
     decode_item<B, BPL, M>(ms, nb, tau, nchunks, kpad, rb, cb, lane, ib, lut, xs, acc);
   if (j + 2 < items)
     decode_item<B, BPL, M>(ms, nb, tau, nchunks, kpad, ra, ca, lane, ia, lut, xs, acc);
+}
+
+// LP2X side channel: after the LP2 kernel (whose records for these blocks are
+// zero), one wave per row adds the blocks LP2 cannot hold.  Lanes take the
+// row's entries in turn and decode them with the LP3 code words; the partial
+// sums are reduced in a fixed order and lane 63 adds s 2^24 times the total
+// to y.  Rows without entries return at once.
+template <int B>
+__global__ void __launch_bounds__(256)
+lp2x_exc_kernel(const uint64_t* __restrict__ table, const uint32_t* __restrict__ exc_off,
+                const uint4* __restrict__ exc, const uint16_t* __restrict__ scale, int rows,
+                int cols, const uint16_t* __restrict__ x, float* __restrict__ y) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int r = __builtin_amdgcn_readfirstlane((int)((blockIdx.x * blockDim.x + threadIdx.x) >> 6));
+  if (r >= rows) return;
+  const uint32_t e0 = exc_off[r], e1 = exc_off[r + 1];
+  if (e0 == e1) return;
+  float acc[B];
+#pragma unroll
+  for (int bb = 0; bb < B; ++bb) acc[bb] = 0.f;
+  for (uint32_t e = e0 + lane; e < e1; e += kWave) {
+    const uint4 ent = exc[e];
+    const int k = (int)(ent.x & 0xFFFFu);
+    const uint2 l = leech_lut(table[ent.x >> 16]);  // never class 0
+    const uint32_t w[3] = {ent.y, ent.z, ent.w};
+#pragma unroll
+    for (int wi = 0; wi < 3; ++wi) {
+#pragma unroll
+      for (int vi = 0; vi < 4; ++vi) {
+        const uint32_t d = leech_pair(w[wi], vi, l.x, l.y);
+        const int c = 24 * k + 8 * wi + 2 * vi;
+#pragma unroll
+        for (int bb = 0; bb < B; ++bb) {
+          const uint16_t* xr = x + (size_t)bb * cols + c;
+          acc[bb] = dot2(d, (uint32_t)xr[0] | ((uint32_t)xr[1] << 16), acc[bb]);
+        }
+      }
+    }
+  }
+  const float s = half_bits_to_float(scale[r]) * 16777216.0f;
+#pragma unroll
+  for (int bb = 0; bb < B; ++bb) {
+    const float tot = wave_sum_lane63(acc[bb]);
+    if (lane == kWave - 1) y[(size_t)bb * rows + r] += tot * s;
+  }
 }
 
 // Rows shorter than one block: y = sum of the unquantized tail only.
@@ -549,6 +633,7 @@ int launch_leech_bpl(const MatSet& ms, int mode, int rows, int cols, const uint1
   if constexpr (gain_bpl_ok(B, BPL)) {
     if (mode == kGain) return launch_leech_mode<B, BPL, kGain>(ms, rows, cols, x, st);
   }
+  if (mode == kLp2) return launch_leech_mode<B, BPL, kLp2>(ms, rows, cols, x, st);
   return launch_leech_mode<B, BPL, kSingle>(ms, rows, cols, x, st);
 }
 
@@ -608,7 +693,8 @@ int single_gemv(const void* blob, int rows, int cols, const uint16_t* x, float* 
   if (rows == 0) return LVQ_OK;
   if (cols == 0) return zero_output(y, (size_t)batch * rows, st);
   MatSet ms = {};
-  ms.v[0] = leech_view(blob, (size_t)rows, (size_t)cols);
+  ms.v[0] = mode == kLp2 ? lp2_view(blob, (size_t)rows, (size_t)cols)
+                         : leech_view(blob, (size_t)rows, (size_t)cols);
   ms.y[0] = y;
   ms.start[0] = 0;
   for (int i = 1; i <= kMaxFused; ++i) ms.start[i] = rows;
@@ -624,6 +710,34 @@ using namespace lvq;
 extern "C" int lvq_gemv(const void* blob, int rows, int cols, const uint16_t* x, float* y,
                         int batch, void* stream) {
   return single_gemv(blob, rows, cols, x, y, batch, stream, kSingle);
+}
+
+extern "C" int lvq_gemv_lp2(const void* blob, int rows, int cols, const uint16_t* x, float* y,
+                            int batch, void* stream) {
+  return single_gemv(blob, rows, cols, x, y, batch, stream, kLp2);
+}
+
+extern "C" int lvq_gemv_lp2x(const void* blob, int rows, int cols, size_t n_exceptions,
+                             const uint16_t* x, float* y, int batch, void* stream) {
+  int e = single_gemv(blob, rows, cols, x, y, batch, stream, kLp2);
+  if (e || rows <= 0 || cols < 24 || n_exceptions == 0) return e;
+  const uint8_t* b = (const uint8_t*)blob;
+  const Sections s = lp2_sections((size_t)rows, (size_t)cols);
+  const Lp2xSections sx = lp2x_sections((size_t)rows, (size_t)cols, n_exceptions);
+  const dim3 grid((unsigned)(((size_t)rows * kWave + 255) / 256)), wg(256);
+  const uint64_t* table = (const uint64_t*)(b + s.table);
+  const uint32_t* off = (const uint32_t*)(b + sx.exc_off);
+  const uint4* ex = (const uint4*)(b + sx.exc);
+  const uint16_t* scale = (const uint16_t*)(b + s.scale);
+  hipStream_t st = (hipStream_t)stream;
+  clear_hip_error();
+  switch (batch) {
+    case 1: hipLaunchKernelGGL(lp2x_exc_kernel<1>, grid, wg, 0, st, table, off, ex, scale, rows, cols, x, y); break;
+    case 2: hipLaunchKernelGGL(lp2x_exc_kernel<2>, grid, wg, 0, st, table, off, ex, scale, rows, cols, x, y); break;
+    case 3: hipLaunchKernelGGL(lp2x_exc_kernel<3>, grid, wg, 0, st, table, off, ex, scale, rows, cols, x, y); break;
+    default: hipLaunchKernelGGL(lp2x_exc_kernel<4>, grid, wg, 0, st, table, off, ex, scale, rows, cols, x, y); break;
+  }
+  return launch_status();
 }
 
 extern "C" int lvq_gemv_gain(const void* blob, int rows, int cols, float gain0, float gain1,

@@ -226,3 +226,50 @@ def unpack_lp2(blob, rows: int, cols: int) -> dict:
     return {"coords": coords.astype(np.int8).reshape(rows, nb, 24), "cls": cls.reshape(rows, nb),
             "scale": buf[off["scale"]: off["scale"] + rows * 2].view("<u2").copy(),
             "tail": buf[off["tail"]: off["tail"] + rows * tau * 2].view("<u2").reshape(rows, tau).copy()}
+
+
+# --------------------------------------------------------------------------
+# LP2X: LP2 plus an exception side channel
+# --------------------------------------------------------------------------
+#
+# After the LP2 sections: exc_off u32 [R + 1] (first entry of each row) and
+# 16-byte entries {block index | class id << 16, the block's three code words
+# in the LP3 packing above}.  Blocks in the side channel have a zero LP2
+# record.
+
+def sections_lp2x(rows: int, cols: int, n_exc: int) -> dict:
+    off = sections_lp2(rows, cols)
+    off["exc_off"] = off["total"]
+    off["exc"] = off["exc_off"] + _align((rows + 1) * 4)
+    off["total"] = off["exc"] + _align(n_exc * 16)
+    return off
+
+
+def unpack_lp2x(blob, rows: int, cols: int, n_exc: int) -> dict:
+    """Coordinates of an LP2X blob: the LP2 records, then every side-channel
+    entry decoded with the LP3 slot layout and the oracle's class table."""
+    buf = np.frombuffer(bytes(blob), dtype=np.uint8)
+    off = sections_lp2x(rows, cols, n_exc)
+    assert buf.size == off["total"], (buf.size, off["total"])
+    nb = cols // 24
+    head = unpack_lp2(buf[: sections_lp2(rows, cols)["total"]].tobytes(), rows, cols)
+    coords = head["coords"].astype(np.int64).reshape(rows * nb, 24) if nb else \
+        np.zeros((0, 24), dtype=np.int64)
+    exc_off = buf[off["exc_off"]: off["exc_off"] + (rows + 1) * 4].view("<u4")
+    ent = buf[off["exc"]: off["exc"] + n_exc * 16].view("<u4").reshape(n_exc, 4)
+    classes = leech.classes()
+    for r in range(rows):
+        for e in range(int(exc_off[r]), int(exc_off[r + 1])):
+            k, cid = int(ent[e, 0] & 0xFFFF), int(ent[e, 0] >> 16)
+            mags = sorted(set(classes[cid]["key"]))
+            x = np.zeros(24, dtype=np.int64)
+            for w in range(3):
+                word = int(ent[e, 1 + w])
+                for slot in range(8):
+                    j = 8 * w + 2 * (slot % 4) + slot // 4
+                    rank = ((word >> (4 * slot)) & 7) - 1
+                    nonneg = (word >> ((4 * slot + 11) % 32)) & 1
+                    x[j] = mags[rank] if nonneg else -mags[rank]
+            assert not np.any(coords[r * nb + k]), "side-channel block with a main record"
+            coords[r * nb + k] = x
+    return {"coords": coords.astype(np.int8).reshape(rows, nb, 24), "exc_off": exc_off.copy()}

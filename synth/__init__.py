@@ -259,14 +259,22 @@ def _shells_low(rng, n):
     return rng.choice(ms, size=n, p=p / p.sum())
 
 
+def _shells_ball(rng, n):
+    ms = np.arange(2, 13)
+    p = 2.0 ** -ms
+    return rng.choice(ms, size=n, p=p / p.sum())
+
+
 def leech_matrix(rows: int, cols: int, cfg: int, key=None, zero_rate: float = None) -> dict:
     """Leech workload: coords int8 [R][nb][24], scale fp16 bits [R],
     tail fp16 bits [R][cols % 24].  cfg 1 uses shells {2,3} and 2% origin
-    blocks; cfg 3, 4 and 5 use shells 2..6 with P(m) ~ 2^-m."""
+    blocks; cfg 3, 4 and 5 use shells 2..6 with P(m) ~ 2^-m; cfg 6 the whole
+    ball, shells 2..12 with P(m) ~ 2^-m (about 1 % of blocks on shells >= 9)."""
     base = [0, cfg] if key is None else [0, cfg] + list(key)
     nb, tau = cols // 24, cols % 24
     r_c = rng_for(*base, ARR_COORDS, rows, cols)
-    shells = _shells_cfg1(r_c, rows * nb) if cfg == 1 else _shells_low(r_c, rows * nb)
+    shells = (_shells_cfg1(r_c, rows * nb) if cfg == 1 else
+              _shells_ball(r_c, rows * nb) if cfg == 6 else _shells_low(r_c, rows * nb))
     coords = sample_shells(shells, r_c).reshape(rows, nb, 24)
     zr = (0.02 if cfg == 1 else 0.0) if zero_rate is None else zero_rate
     if zr:

@@ -339,3 +339,41 @@ def test_expand_lp2_every_small_class_and_the_refusals():
         lvq.expand_lp2(x, synth.fp16_bits(np.ones(2)), None, 2, 48)
     assert e.value.code == lvq.LVQ_E_LAYOUT and e.value.index == (1, 1)
     assert lvq.strerror(lvq.LVQ_E_LAYOUT).startswith("a block's class")
+
+
+def _all_class_coords(rows, nb, seed):
+    rng = np.random.default_rng(seed)
+    ids = rng.integers(0, leech.NUM_CLASSES, rows * nb)
+    cl = leech.classes()
+    coords = np.zeros((rows * nb, 24), dtype=np.int8)
+    for cid in np.unique(ids):
+        sel = np.nonzero(ids == cid)[0]
+        if cid:
+            coords[sel] = synth.sample_class(cl[cid]["key"], sel.size, rng)
+    return coords.reshape(rows, nb, 24), ids
+
+
+@pytest.mark.parametrize("src", ["ball", "all_classes"])
+def test_expand_lp2x_round_trips_through_the_oracle_unpacker(src):
+    if src == "ball":
+        rows, cols = 40, 24 * 200 + 7
+        d = synth.leech_matrix(rows, cols, 6, key=(40,))
+        coords, scale, tail = d["coords"], d["scale"], d["tail"]
+        ids = np.array([leech.class_of(b) for b in coords.reshape(-1, 24)])
+    else:
+        rows, nb = 30, 50
+        cols = 24 * nb
+        coords, ids = _all_class_coords(rows, nb, 3)
+        scale, tail = synth.fp16_bits(np.ones(rows)), None
+    cl = leech.classes()
+    want_exc = int(sum(1 for i in ids if i >= 256 or len(set(cl[i]["key"])) > 4))
+    blob, n_exc = lvq.expand_lp2x(coords, scale, tail, rows, cols)
+    assert n_exc == want_exc and (n_exc > 0)
+    assert blob.size == lvq.library().lvq_layout_bytes_lp2x(rows, cols, n_exc)
+    u = layout.unpack_lp2x(blob, rows, cols, n_exc)
+    assert np.array_equal(u["coords"], coords)
+    # a wrong count is refused
+    bad = np.empty(lvq.library().lvq_layout_bytes_lp2x(rows, cols, n_exc + 1), dtype=np.uint8)
+    assert lvq.library().lvq_expand_lp2x(coords.ctypes.data, scale.ctypes.data,
+                                         None if tail is None else tail.ctypes.data, rows, cols,
+                                         n_exc + 1, bad.ctypes.data) == lvq.LVQ_E_SHAPE
