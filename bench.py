@@ -254,10 +254,14 @@ class Bench:
             "copies": copies, "reps": self.args.steps, "trials": self.args.trials, "graph": False,
         }
         r.update(extra)
+        note = ""
+        if "us_noweights" in extra:
+            note = "  (no weights %.3f us)" % extra["us_noweights"]
+        if "us_rotate_then_gemv" in extra:
+            note = "  (rotate + gemv: %.3f us)" % extra["us_rotate_then_gemv"]
         log("%-8s cfg%s %5dx%-5d b%d: %7.3f us  %7.1f GB/s  %5.1f%% peak  %5.1f%% of stream%s"
             % (arm, cfg, rows, cols, batch, us, gbps, r["pct_hbm_peak"], r["pct_stream_ceiling"],
-               "" if "us_noweights" not in extra else "  (no weights %.3f us)"
-               % extra["us_noweights"]))
+               note))
         return r
 
     # one Leech matrix at one shape and batch
@@ -445,6 +449,34 @@ class Bench:
         del bufs
         torch.cuda.empty_cache()
         return self.record("leech_gain", 4, rows, cols, batch, leech_bytes(rows, cols), n, tm)
+
+    def rotated_gemv(self, rows, cols, m, batch):
+        """Rotation fused into the GEMV against the two launches it replaces."""
+        import numpy as np
+        import synth
+        torch, lvq = self.torch, self.lvq
+        d = synth.leech_matrix(rows, cols, 3)
+        blob = lvq.expand(d["coords"], d["scale"], d["tail"], rows, cols)
+        rng = np.random.default_rng(cols + m)
+        x = synth.activations(cols, batch, 3, rows=rows)
+        words = rng.integers(0, 1 << 32, (cols + 31) // 32, dtype=np.uint64).astype(np.uint32)
+        q = np.linalg.qr(rng.standard_normal((m, m)))[0].astype(np.float32) if m > 1 else None
+        n = copies_for(blob.size)
+        bufs = dev_copies(torch, blob, n)
+        xd, wd = to_dev(torch, x), to_dev(torch, words)
+        qd = None if q is None else torch.from_numpy(q).cuda()
+        xr = torch.empty((batch, cols), dtype=torch.int16, device="cuda")
+        yd = torch.empty((batch, rows), dtype=torch.float32, device="cuda")
+        tf = self.time(lambda i: lvq.gemv_rotated(bufs[i % n], rows, cols, wd, qd, m, xd, yd, batch))
+
+        def two(i):
+            lvq.rotate(xd, cols, m, wd, qd, xr, batch)
+            lvq.gemv(bufs[i % n], rows, cols, xr, yd, batch)
+        t2 = Timed(torch, two, self.args.steps, self.args.warmup, self.args.trials, enqueue_ms=0.08)
+        del bufs
+        torch.cuda.empty_cache()
+        return self.record("leech_rot", 3, rows, cols, batch, leech_bytes(rows, cols), n, tf,
+                           rot_m=m, us_rotate_then_gemv=round(t2.median, 3))
 
     def rotate(self, n, m, batch):
         """The activation rotation (H kron Q)(S x) at width n = K m."""
@@ -751,6 +783,9 @@ def main():
         for n, m in ((4096, 1), (12288, 3), (25600, 25)):
             records.append(B.rotate(n, m, 1))
         records.append(B.rotate(12288, 3, 4))
+        records.append(B.rotated_gemv(4096, 12288, 3, 1))
+        records.append(B.rotated_gemv(4096, 4096, 1, 1))
+        records.append(B.rotated_gemv(12288, 4096, 1, 1))
         records.append(B.leech_gain(ROWS, COLS, 1))
         records.append(B.leech_lp2(4, ROWS, COLS, 1, d=d))
         records.append(B.leech_lp2(4, ROWS, COLS, 4, d=d))

@@ -77,6 +77,7 @@ def _load():
         "trellis_gemv": (i, [vp, vp, vp, i, i, vp, vp, i, vp]),
         "fp16_gemv": (i, [vp, i, i, vp, vp, i, vp]),
         "lvq_rotate": (i, [vp, vp, vp, i, i, vp, i, vp]),
+        "lvq_gemv_rotated": (i, [vp, i, i, vp, vp, i, vp, vp, i, vp]),
         "lvq_stream_read": (i, [vp, sz, vp, vp]),
     }
     for name, (res, args) in sig.items():
@@ -93,7 +94,8 @@ EXPORTED = ("lvq_strerror", "lvq_last_error_index", "lvq_class_table", "lvq_layo
             "lvq_gemv_lp2x",
             "lvq_rank", "lvq_gemv", "lvq_gemv_gain",
             "lvq_unfold", "lvq_gemv_fused", "lvq_gemv_noweights", "lvq_decode",
-            "bpdq_gemv", "trellis_gemv", "fp16_gemv", "lvq_rotate", "lvq_stream_read")
+            "bpdq_gemv", "trellis_gemv", "fp16_gemv", "lvq_rotate", "lvq_gemv_rotated",
+            "lvq_stream_read")
 
 
 def library():
@@ -323,6 +325,13 @@ def rotate(x, n: int, m: int, sign_words, q, y, batch: int = 1, stream=None):
     """y = (H kron Q)(S x) per batch row (fp16 in, fp16 out; y may be x)."""
     _check(_lib.lvq_rotate(_ptr(x), _ptr(sign_words), _ptr(q), int(n), int(m), _ptr(y),
                            int(batch), _stream(stream)))
+
+
+def gemv_rotated(blob, rows: int, cols: int, sign_words, q, m: int, x, y, batch: int = 1,
+                 stream=None):
+    """y = W (H kron Q)(S x) in one launch (the rotation of rotate())."""
+    _check(_lib.lvq_gemv_rotated(_ptr(blob), int(rows), int(cols), _ptr(sign_words), _ptr(q),
+                                 int(m), _ptr(x), _ptr(y), int(batch), _stream(stream)))
 
 
 def stream_read(buf, nbytes: int, sink, stream=None):

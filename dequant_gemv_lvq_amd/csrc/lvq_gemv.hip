@@ -27,6 +27,7 @@
 // result does not depend on timing.
 
 #include "common.h"
+#include "rotate_dev.h"
 #include "layout.h"
 
 namespace lvq {
@@ -138,13 +139,19 @@ constexpr int kMaxFused = 4;
 // kGain: one matrix whose class ids carry a shape-gain bit in bit 15; the
 // block's weights are multiplied by gain[bit]
 // kLp2: one matrix in the LP2 layout (two rank planes, class in the record)
-constexpr int kSingle = 0, kFused = 1, kNoWeights = 2, kGain = 3, kLp2 = 4;
+// kRot: one matrix whose input is first rotated, (H kron Q)(S x), in LDS
+constexpr int kSingle = 0, kFused = 1, kNoWeights = 2, kGain = 3, kLp2 = 4, kRot = 5;
 
 struct MatSet {
   LeechView v[kMaxFused];
   float* y[kMaxFused];
   int start[kMaxFused + 1];
   float gain[2];
+  // kRot: the rotation of x (see lvq_rotate)
+  const uint32_t* rot_signs;
+  const float* rot_q;
+  int rot_m, rot_logk;
+  float rot_scale;
 };
 
 template <int M>
@@ -361,10 +368,119 @@ __device__ __forceinline__ uint2 stage_lut(int c, uint64_t entry) {
 // Waves per SIMD the register allocation must leave room for: 8 (at most 64
 // VGPRs, two 1024-thread workgroups per CU) for the variants that fit there
 // without spilling, and whatever the allocation gives for the larger ones.
-// (The shape-gain mode keeps a partial sum per word and goes without, and so
-// does LP2 above batch 1, whose class extraction needs the registers.)
+// (The shape-gain mode keeps a partial sum per word and goes without, as do
+// the rotating mode, whose prologue holds 16-value butterfly sets, and LP2
+// above batch 1, whose class extraction needs the registers.)
 constexpr int leech_min_waves(int B, int BPL, int M) {
-  return M != kGain && !(M == kLp2 && B > 1) && B + BPL <= 4 ? 8 : 1;
+  return M != kGain && M != kRot && !(M == kLp2 && B > 1) && B + BPL <= 4 ? 8 : 1;
+}
+
+// Stages s .. s + R - 1 of every sequence of the f32 buffer fb (the m
+// sequences of K values one after another): coordinates 2^s apart.  The first
+// pass (s = 0, m = 1) reads the staged fp16 x with its signs instead; the last
+// scales, rounds and writes fp16 back to x at c m + b.
+template <int R>
+__device__ __forceinline__ void rot_lds_pass(uint16_t* xh, float* fb, const uint32_t* signs,
+                                             int k, int m, int s, bool first, bool last,
+                                             float scale, int tid, int nthr) {
+  constexpr int kR = 1 << R;
+  const int low = (1 << s) - 1;
+  const int nsets = k >> R;
+  for (int sg = tid; sg < m * nsets; sg += nthr) {
+    const int b = m == 1 ? 0 : sg / nsets;
+    const int set = sg - b * nsets;
+    const int c0 = ((set & ~low) << R) | (set & low);
+    float v[kR];
+    if (first && kR == 16) {  // m == 1, s == 0: 16 consecutive fp16 of x, two 16-byte reads
+      const uint32_t s16 = signs ? signs[c0 >> 5] >> (c0 & 31) : 0u;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const uint4 u = rot_apply_signs(*(const uint4*)(xh + c0 + 8 * h), s16 >> (8 * h));
+        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          v[8 * h + 2 * i] = rot_half((uint16_t)w[i]);
+          v[8 * h + 2 * i + 1] = rot_half((uint16_t)(w[i] >> 16));
+        }
+      }
+    } else if (first) {  // fewer than 16: element by element
+#pragma unroll
+      for (int t = 0; t < kR; ++t) v[t] = rot_half(xh[c0 + t] ^ rot_sign_bit(signs, c0 + t));
+    } else {
+#pragma unroll
+      for (int t = 0; t < kR; ++t) v[t] = fb[b * k + c0 + (t << s)];
+    }
+    rot_set_stages<R>(v);
+    if (last) {
+#pragma unroll
+      for (int t = 0; t < kR; ++t) xh[(c0 + (t << s)) * m + b] = rot_out(v[t], scale);
+    } else {
+#pragma unroll
+      for (int t = 0; t < kR; ++t) fb[b * k + c0 + (t << s)] = v[t];
+    }
+  }
+}
+
+// One batch row of the staged x (fp16, in LDS, zero past cols) rotated in
+// place.  The butterflies are lvq_rotate's, stage by stage in the same order on
+// the same operands (only where the values live differs), and so is the Q mix,
+// so the result is that kernel's output bit for bit.  Q mix: a thread takes
+// whole groups of m coordinates, the Q row entries are uniform (scalar loads);
+// then radix-16 passes over the K-point sequences in LDS, one barrier each.
+// Every thread of the workgroup takes part; ends with a barrier.
+__device__ void rotate_x_lds(uint16_t* xh, float* fb, const float* qs, const uint32_t* signs,
+                             const MatSet& ms, int cols, int tid, int nthr) {
+  // qs and signs are the LDS copies (or null); no global load here, so
+  // nothing waits on the weight loads in flight
+  const int m = ms.rot_m, logk = ms.rot_logk;
+  const int k = cols / m;
+  float scale = ms.rot_scale;
+  if (m == 1 && qs) scale *= qs[0];
+  if (m > 1) {
+    for (int c = tid; c < k; c += nthr) {
+      float xv[8];
+      const bool small = m <= 8;  // uniform
+      if (small) {
+#pragma unroll
+        for (int d = 0; d < 8; ++d) {
+          const int j = c * m + d;
+          xv[d] = d < m ? rot_half(xh[j] ^ rot_sign_bit(signs, j)) : 0.f;
+        }
+      }
+      for (int b = 0; b < m; ++b) {
+        float a = 0.f;
+        if (small) {
+#pragma unroll
+          for (int d = 0; d < 8; ++d)
+            if (d < m) a = __builtin_fmaf(qs ? qs[b * m + d] : (d == b ? 1.f : 0.f), xv[d], a);
+        } else {
+          for (int d = 0; d < m; ++d) {
+            const int j = c * m + d;
+            a = __builtin_fmaf(qs ? qs[b * m + d] : (d == b ? 1.f : 0.f),
+                               rot_half(xh[j] ^ rot_sign_bit(signs, j)), a);
+          }
+        }
+        fb[b * k + c] = a;
+      }
+    }
+    __syncthreads();
+  }
+  for (int s = 0; s < logk; s += 4) {
+    const int r = logk - s < 4 ? logk - s : 4;
+    const bool first = s == 0 && m == 1, last = s + r == logk;
+    if (r == 4) rot_lds_pass<4>(xh, fb, signs, k, m, s, first, last, scale, tid, nthr);
+    else if (r == 3) rot_lds_pass<3>(xh, fb, signs, k, m, s, first, last, scale, tid, nthr);
+    else if (r == 2) rot_lds_pass<2>(xh, fb, signs, k, m, s, first, last, scale, tid, nthr);
+    else rot_lds_pass<1>(xh, fb, signs, k, m, s, first, last, scale, tid, nthr);
+    __syncthreads();
+  }
+  if (logk == 0) {  // K = 1: y = scale Q x, nothing but the mix
+    for (int c = tid; c < cols; c += nthr) {
+      const float v = m == 1 ? rot_half(xh[c] ^ rot_sign_bit(signs, c)) : fb[c];
+      xh[c] = rot_out(v, scale);
+    }
+    __syncthreads();
+  }
 }
 
 template <int B, int BPL, int M>
@@ -410,6 +526,35 @@ leech_gemv_kernel(MatSet ms, int rows, int nb, int tau, int cols, int nchunks, i
       xh[i] = c < cols ? x[(size_t)bb * cols + c] : (uint16_t)0;
     }
   }
+  // kRot: LDS after x holds the f32 rotation buffer [cols], then Q [m][m] and
+  // the sign words, each rounded up to 256 bytes (one 4-byte-per-lane copy);
+  // Q and the signs come in by buffer-to-LDS loads issued before the weight
+  // loads, so the barrier below waits for them and the rotation makes no
+  // global load
+  float* fb = (float*)((uint8_t*)xs + (size_t)B * kpad * 2);
+  float* qs = nullptr;
+  uint32_t* sw = nullptr;
+  if (M == kRot) {
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    uint8_t* p = (uint8_t*)fb + (((size_t)cols * 4 + 15) & ~(size_t)15);
+    if (ms.rot_q) {
+      qs = (float*)p;
+      const uint32_t qb = (uint32_t)(ms.rot_m * ms.rot_m * 4);
+      const auto rq = buffer_rsrc(ms.rot_q, qb);
+      for (uint32_t q = wv; q * 256 < qb; q += wpb)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rq, (__attribute__((address_space(3))) void*)(p + q * 256), 4, lane * 4, q * 256, 0, 0);
+      p += (qb + 255) & ~255u;
+    }
+    if (ms.rot_signs) {
+      sw = (uint32_t*)p;
+      const uint32_t sb = (uint32_t)((cols + 31) / 32 * 4);
+      const auto rs = buffer_rsrc(ms.rot_signs, sb);
+      for (uint32_t q = wv; q * 256 < sb; q += wpb)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rs, (__attribute__((address_space(3))) void*)(p + q * 256), 4, lane * 4, q * 256, 0, 0);
+    }
+  }
   const uint64_t* table = ms.v[0].table;  // the same universal table in every blob
   const uint64_t te = table[min(tid, LVQ_NUM_CLASSES - 1)];
   asm volatile("" ::: "memory");
@@ -429,6 +574,12 @@ leech_gemv_kernel(MatSet ms, int rows, int nb, int tau, int cols, int nchunks, i
     lut[c] = M == kLp2 ? stage_lut_lp2(e) : stage_lut(c, e);
   }
   __syncthreads();
+  if (M == kRot) {
+    // the first items' weight loads stay in flight meanwhile
+#pragma unroll
+    for (int bb = 0; bb < B; ++bb)
+      rotate_x_lds((uint16_t*)xs + (size_t)bb * kpad, fb, qs, sw, ms, cols, tid, nthr);
+  }
 
   float acc[B][3];
 #pragma unroll
@@ -596,7 +747,12 @@ int launch_leech_mode(const MatSet& ms, int rows, int cols, const uint16_t* x, h
   const size_t npad = (size_t)nchunks * kWave * BPL;
   size_t kpad = npad * 24 > (size_t)cols ? npad * 24 : (size_t)cols;
   kpad = (kpad + 511) & ~(size_t)511;
-  const size_t lds = (size_t)LVQ_NUM_CLASSES * 8 + (size_t)B * kpad * 2;
+  size_t lds = (size_t)LVQ_NUM_CLASSES * 8 + (size_t)B * kpad * 2;
+  if (M == kRot) {
+    lds += ((size_t)cols * 4 + 15) & ~(size_t)15;
+    if (ms.rot_q) lds += ((size_t)ms.rot_m * ms.rot_m * 4 + 255) & ~(size_t)255;
+    if (ms.rot_signs) lds += ((size_t)(cols + 31) / 32 * 4 + 255) & ~(size_t)255;
+  }
   if (lds > device_lds_bytes()) return LVQ_E_SHAPE;
   const int cus = device_cus();
   const int threads = wg_threads(rows, cus);
@@ -621,8 +777,8 @@ int launch_leech_mode(const MatSet& ms, int rows, int cols, const uint16_t* x, h
   return launch_status();
 }
 
-// the shape-gain mode's extra partial sums do not fit 4 blocks per lane at
-// batch 2 (launch_leech never asks for it)
+// the shape-gain mode's extra partial sums, and the rotating mode's prologue,
+// do not fit 4 blocks per lane at batch 2 (launch_leech never asks for it)
 constexpr bool gain_bpl_ok(int B, int BPL) { return !(B >= 2 && BPL >= 4); }
 
 template <int B, int BPL>
@@ -634,6 +790,9 @@ int launch_leech_bpl(const MatSet& ms, int mode, int rows, int cols, const uint1
     if (mode == kGain) return launch_leech_mode<B, BPL, kGain>(ms, rows, cols, x, st);
   }
   if (mode == kLp2) return launch_leech_mode<B, BPL, kLp2>(ms, rows, cols, x, st);
+  if constexpr (gain_bpl_ok(B, BPL)) {
+    if (mode == kRot) return launch_leech_mode<B, BPL, kRot>(ms, rows, cols, x, st);
+  }
   return launch_leech_mode<B, BPL, kSingle>(ms, rows, cols, x, st);
 }
 
@@ -660,14 +819,26 @@ int launch_leech(const MatSet& ms, int n, int mode, int rows, int cols, const ui
     }
     return LVQ_OK;
   }
-  const int bpl = choose_bpl(nb, mode == kGain && B >= 2 ? 3 : max_bpl(B), rows, device_cus());
+  const int bpl =
+      choose_bpl(nb, (mode == kGain || mode == kRot) && B >= 2 ? 3 : max_bpl(B), rows, device_cus());
   if constexpr (max_bpl(B) >= 4) {
-    if (bpl == 4) return launch_leech_bpl<B, 4>(ms, mode, rows, cols, x, st);
+    if (bpl == 4) {
+      const int e = launch_leech_bpl<B, 4>(ms, mode, rows, cols, x, st);
+      if (!(e == LVQ_E_SHAPE && mode == kRot)) return e;
+    }
   }
   if constexpr (max_bpl(B) >= 3) {
-    if (bpl == 3) return launch_leech_bpl<B, 3>(ms, mode, rows, cols, x, st);
+    if (bpl == 3) {
+      const int e = launch_leech_bpl<B, 3>(ms, mode, rows, cols, x, st);
+      if (!(e == LVQ_E_SHAPE && mode == kRot)) return e;
+    }
   }
-  if (bpl == 2) return launch_leech_bpl<B, 2>(ms, mode, rows, cols, x, st);
+  if (bpl == 2) {
+    const int e = launch_leech_bpl<B, 2>(ms, mode, rows, cols, x, st);
+    // the rotating mode's LDS can miss by the padding of x; one block per
+    // lane pads least (the size check fails before anything is launched)
+    if (!(e == LVQ_E_SHAPE && mode == kRot)) return e;
+  }
   return launch_leech_bpl<B, 1>(ms, mode, rows, cols, x, st);
 }
 
@@ -681,8 +852,16 @@ int launch_set(const MatSet& ms, int n, int mode, int rows, int cols, const uint
   }
 }
 
+struct RotArgs {
+  const uint32_t* signs = nullptr;
+  const float* q = nullptr;
+  int m = 1, logk = 0;
+  float scale = 1.f;
+};
+
 int single_gemv(const void* blob, int rows, int cols, const uint16_t* x, float* y, int batch,
-                void* stream, int mode, float gain0 = 1.f, float gain1 = 1.f) {
+                void* stream, int mode, float gain0 = 1.f, float gain1 = 1.f,
+                const RotArgs& rot = RotArgs()) {
   if (rows < 0 || cols < 0) return LVQ_E_SHAPE;
   int e = check_batch(batch);
   if (e) return e;
@@ -700,6 +879,11 @@ int single_gemv(const void* blob, int rows, int cols, const uint16_t* x, float* 
   for (int i = 1; i <= kMaxFused; ++i) ms.start[i] = rows;
   ms.gain[0] = gain0;
   ms.gain[1] = gain1;
+  ms.rot_signs = rot.signs;
+  ms.rot_q = rot.q;
+  ms.rot_m = rot.m;
+  ms.rot_logk = rot.logk;
+  ms.rot_scale = rot.scale;
   return launch_set(ms, 1, mode, rows, cols, x, batch, st);
 }
 
@@ -715,6 +899,23 @@ extern "C" int lvq_gemv(const void* blob, int rows, int cols, const uint16_t* x,
 extern "C" int lvq_gemv_lp2(const void* blob, int rows, int cols, const uint16_t* x, float* y,
                             int batch, void* stream) {
   return single_gemv(blob, rows, cols, x, y, batch, stream, kLp2);
+}
+
+extern "C" int lvq_gemv_rotated(const void* blob, int rows, int cols, const uint32_t* sign_words,
+                                const float* q, int m, const uint16_t* x, float* y, int batch,
+                                void* stream) {
+  if (m < 1 || m > 32 || cols < 24 || cols % m) return cols < 0 ? LVQ_E_SHAPE : LVQ_E_SHAPE;
+  const int k = cols / m;
+  if (k & (k - 1)) return LVQ_E_SHAPE;
+  RotArgs rot;
+  while ((1 << rot.logk) < k) ++rot.logk;
+  if (rot.logk > 15) return LVQ_E_SHAPE;
+  if (!aligned16(sign_words) || !aligned16(q)) return LVQ_E_ALIGN;
+  rot.signs = sign_words;
+  rot.q = q;
+  rot.m = m;
+  rot.scale = (float)(1.0 / __builtin_sqrt((double)k));
+  return single_gemv(blob, rows, cols, x, y, batch, stream, kRot, 1.f, 1.f, rot);
 }
 
 extern "C" int lvq_gemv_lp2x(const void* blob, int rows, int cols, size_t n_exceptions,

@@ -31,33 +31,16 @@
 // f32), takes 54 KiB.
 
 #include "common.h"
+#include "rotate_dev.h"
 
 namespace lvq {
 
 constexpr int kRotThreads = 1024;
 constexpr int kRotMaxM = 32;
 
-__device__ __forceinline__ float rot_half(uint16_t h) {
-  return (float)__builtin_bit_cast(_Float16, h);
-}
 
-// the sign bits of 8 consecutive coordinates (bits 0..7) onto fp16 sign bits
-__device__ __forceinline__ uint4 rot_apply_signs(uint4 v, uint32_t s8) {
-  auto two = [](uint32_t w, uint32_t b2) {
-    return w ^ (((b2 & 1u) << 15) | ((b2 & 2u) << 30));
-  };
-  return make_uint4(two(v.x, s8), two(v.y, s8 >> 2), two(v.z, s8 >> 4), two(v.w, s8 >> 6));
-}
 
-// Butterfly over lane bit `mask`: the lower lane keeps a + b, the upper b' = a - b.
-__device__ __forceinline__ float rot_lane_bfly(float v, int mask, int lane) {
-  const float o = __shfl_xor(v, mask, kWave);
-  return (lane & mask) ? o - v : v + o;
-}
 
-__device__ __forceinline__ uint16_t rot_out(float v, float scale) {
-  return __builtin_bit_cast(uint16_t, (_Float16)(v * scale));
-}
 
 // Stages s .. s + R - 1 (s >= 9) over buf: coordinates 2^s apart, consecutive
 // threads at consecutive addresses.  The last pass scales, rounds and stores.

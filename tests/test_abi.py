@@ -377,3 +377,18 @@ def test_expand_lp2x_round_trips_through_the_oracle_unpacker(src):
     assert lvq.library().lvq_expand_lp2x(coords.ctypes.data, scale.ctypes.data,
                                          None if tail is None else tail.ctypes.data, rows, cols,
                                          n_exc + 1, bad.ctypes.data) == lvq.LVQ_E_SHAPE
+
+
+def test_gemv_rotated_validates_before_launch():
+    lib = lvq.library()
+    A = 1 << 20
+    g = lib.lvq_gemv_rotated
+    assert g(A, 4, 4096, None, None, 0, A, A, 1, None) == lvq.LVQ_E_SHAPE    # m = 0
+    assert g(A, 4, 4096, None, None, 33, A, A, 1, None) == lvq.LVQ_E_SHAPE   # m > 32
+    assert g(A, 4, 4096, None, None, 3, A, A, 1, None) == lvq.LVQ_E_SHAPE    # cols % m
+    assert g(A, 4, 24 * 12, None, None, 1, A, A, 1, None) == lvq.LVQ_E_SHAPE  # K = 288
+    assert g(A, 4, 16, None, None, 1, A, A, 1, None) == lvq.LVQ_E_SHAPE     # no whole block
+    assert g(A, 4, 4096, A + 4, None, 1, A, A, 1, None) == lvq.LVQ_E_ALIGN
+    assert g(A, 4, 3 * 1024, None, A + 8, 3, A, A, 1, None) == lvq.LVQ_E_ALIGN
+    assert g(A, 4, 4096, None, None, 1, A, A, 0, None) == lvq.LVQ_E_BATCH
+    assert g(A, 0, 4096, None, None, 1, A, A, 1, None) == lvq.LVQ_OK

@@ -90,3 +90,32 @@ def test_rotate_in_place_and_exact_cases():
     a = x1.view(np.float16).astype(np.float64)
     b = y1.view(np.float16).astype(np.float64)
     assert np.all(np.abs(a - b) <= 2 * orot.ulp16(a) + 1e-3)
+
+
+@pytest.mark.parametrize("rows,n,m,batch", [
+    (4096, 4096, 1, 1), (4096, 12288, 3, 1), (4096, 12288, 3, 4), (1024, 25600, 25, 1),
+    (300, 2560, 5, 2), (257, 1024 * 19, 19, 1), (64, 256, 1, 3), (96, 24 * 64, 3, 2),
+])
+def test_gemv_rotated_equals_rotate_then_gemv(rows, n, m, batch):
+    import synth as sy
+    from oracle import gemv as og
+    d = sy.leech_matrix(rows, n, 3, key=(rows, n, m))
+    blob = to_dev(lvq.expand(d["coords"], d["scale"], d["tail"], rows, n))
+    x, words, qm = _case(n, m, batch, seed=rows + n)
+    wd = to_dev(words)
+    qd = None if qm is None else to_dev(qm)
+    xr = empty((batch, n), np.uint16)
+    lvq.rotate(to_dev(x), n, m, wd, qd, xr, batch)
+    y_sep = empty((batch, rows), np.float32)
+    lvq.gemv(blob, rows, n, xr, y_sep, batch)
+    y_fused = empty((batch, rows), np.float32)
+    lvq.gemv_rotated(blob, rows, n, wd, qd, m, to_dev(x), y_fused, batch)
+    a, b = to_host(y_fused, np.float32), to_host(y_sep, np.float32)
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+    # and against the oracle: the rotated x as the device rounded it, then f64
+    w = og.leech_weights(d["coords"], d["scale"], d["tail"], n)
+    y64, bound = og.gemv(w, to_host(xr, np.uint16))
+    assert og.check(a, y64, bound) <= 1.0
+    # the rotated x itself against the rotation oracle
+    y64r, bnd = orot.rotate(x, n, m, words, None if qm is None else qm.astype(np.float64))
+    assert orot.rotate_check(to_host(xr, np.uint16), y64r, bnd) <= 1.0
