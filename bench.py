@@ -201,6 +201,14 @@ def lp2_bytes(rows, cols):
     return rows * (12 * nb + 2 + 2 * tau)
 
 
+def direct_bytes(rows, cols):
+    """Direct layout: 16 B per 24-weight block (parity, three magnitude bits
+    and a sign per coordinate, no class), 2 B per row for the scale, 2 B per
+    unquantized tail column."""
+    nb, tau = cols // 24, cols % 24
+    return rows * (16 * nb + 2 + 2 * tau)
+
+
 def bpdq_bytes(rows, cols):
     return (cols // 16) * rows * 4 + (cols // 256) * 3 * rows * 2
 
@@ -410,6 +418,24 @@ class Bench:
         del bufs
         torch.cuda.empty_cache()
         return self.record("leech_lp2", cfg, rows, cols, batch, lp2_bytes(rows, cols), n, tm,
+                           blob_bytes=int(blob.size))
+
+    def leech_direct(self, cfg, rows, cols, batch, d=None):
+        """The table-free direct layout (|x| = 2e + parity) at one shape."""
+        import synth
+        torch, lvq = self.torch, self.lvq
+        if d is None:
+            d = synth.leech_matrix(rows, cols, cfg)
+        blob = lvq.expand_direct(d["coords"], d["scale"], d["tail"], rows, cols)
+        x = synth.activations(cols, batch, cfg, rows=rows)
+        n = copies_for(blob.size)
+        bufs = dev_copies(torch, blob, n)
+        xd = to_dev(torch, x)
+        yd = torch.empty((batch, rows), dtype=torch.float32, device="cuda")
+        tm = self.time(lambda i: lvq.gemv_direct(bufs[i % n], rows, cols, xd, yd, batch))
+        del bufs
+        torch.cuda.empty_cache()
+        return self.record("leech_direct", cfg, rows, cols, batch, direct_bytes(rows, cols), n, tm,
                            blob_bytes=int(blob.size))
 
     def leech_lp2x(self, cfg, rows, cols, batch, d=None):
@@ -794,6 +820,10 @@ def main():
         d6 = __import__("synth").leech_matrix(ROWS, COLS, 6)
         records.append(B.leech(6, ROWS, COLS, 1, d=d6))
         records.append(B.leech_lp2x(6, ROWS, COLS, 1, d=d6))
+        records.append(B.leech_direct(6, ROWS, COLS, 1, d=d6))
+        records.append(B.leech_direct(4, ROWS, COLS, 1, d=d))
+        records.append(B.leech_direct(4, ROWS, COLS, 4, d=d))
+        records.append(B.leech_direct(3, 12288, 4096, 1))
         records.append(B.unfold(ROWS * (COLS // 24)))
         fp16_by_shape = {(r["R"], r["K"]): r["gbps"] for r in records if r["arm"] == "fp16"}
         for r in records:

@@ -66,6 +66,9 @@ def _load():
         "lvq_layout_bytes_lp2x": (sz, [i, i, sz]),
         "lvq_expand_lp2x": (i, [vp, vp, vp, i, i, sz, vp]),
         "lvq_gemv_lp2x": (i, [vp, i, i, sz, vp, vp, i, vp]),
+        "lvq_layout_bytes_direct": (sz, [i, i]),
+        "lvq_expand_direct": (i, [vp, vp, vp, i, i, vp]),
+        "lvq_gemv_direct": (i, [vp, i, i, vp, vp, i, vp]),
         "lvq_rank": (i, [vp, sz, vp]),
         "lvq_unfold": (i, [vp, sz, vp, vp, vp]),
         "lvq_gemv_gain": (i, [vp, i, i, ctypes.c_float, ctypes.c_float, vp, vp, i, vp]),
@@ -91,7 +94,7 @@ _lib = _load()
 EXPORTED = ("lvq_strerror", "lvq_last_error_index", "lvq_class_table", "lvq_layout_bytes",
             "lvq_expand", "lvq_expand_gain", "lvq_layout_bytes_lp2", "lvq_expand_lp2",
             "lvq_gemv_lp2", "lvq_lp2x_exceptions", "lvq_layout_bytes_lp2x", "lvq_expand_lp2x",
-            "lvq_gemv_lp2x",
+            "lvq_gemv_lp2x", "lvq_layout_bytes_direct", "lvq_expand_direct", "lvq_gemv_direct",
             "lvq_rank", "lvq_gemv", "lvq_gemv_gain",
             "lvq_unfold", "lvq_gemv_fused", "lvq_gemv_noweights", "lvq_decode",
             "bpdq_gemv", "trellis_gemv", "fp16_gemv", "lvq_rotate", "lvq_gemv_rotated",
@@ -197,6 +200,28 @@ def expand_lp2(coords, scale, tail, rows: int, cols: int) -> np.ndarray:
     return blob
 
 
+def layout_bytes_direct(rows: int, cols: int) -> int:
+    return int(_lib.lvq_layout_bytes_direct(int(rows), int(cols)))
+
+
+def expand_direct(coords, scale, tail, rows: int, cols: int) -> np.ndarray:
+    """Host expansion into the direct layout (|x| = 2e + parity, no table)."""
+    coords = np.ascontiguousarray(coords, dtype=np.int8)
+    scale = np.ascontiguousarray(scale, dtype=np.uint16)
+    tau = cols % 24
+    tail = None if tau == 0 else np.ascontiguousarray(tail, dtype=np.uint16)
+    if rows < 0 or cols < 0 or coords.size != rows * (cols // 24) * 24:
+        _check(LVQ_E_SHAPE)
+    blob = np.empty(_lib.lvq_layout_bytes_direct(int(rows), int(cols)), dtype=np.uint8)
+    code = _lib.lvq_expand_direct(_ptr(coords), _ptr(scale), _ptr(tail), int(rows), int(cols),
+                                  blob.ctypes.data)
+    if code != LVQ_OK:
+        r, b = ctypes.c_int(), ctypes.c_int()
+        _lib.lvq_last_error_index(ctypes.byref(r), ctypes.byref(b))
+        _check(code, (r.value, b.value))
+    return blob
+
+
 def expand_lp2x(coords, scale, tail, rows: int, cols: int) -> tuple:
     """Host expansion into LP2X; returns (blob, number of side-channel blocks)."""
     coords = np.ascontiguousarray(coords, dtype=np.int8)
@@ -281,6 +306,11 @@ def gemv_noweights(blob, rows: int, cols: int, x, y, batch: int = 1, stream=None
 def gemv_lp2(blob, rows: int, cols: int, x, y, batch: int = 1, stream=None):
     _check(_lib.lvq_gemv_lp2(_ptr(blob), int(rows), int(cols), _ptr(x), _ptr(y), int(batch),
                              _stream(stream)))
+
+
+def gemv_direct(blob, rows: int, cols: int, x, y, batch: int = 1, stream=None):
+    _check(_lib.lvq_gemv_direct(_ptr(blob), int(rows), int(cols), _ptr(x), _ptr(y), int(batch),
+                                _stream(stream)))
 
 
 def gemv_lp2x(blob, rows: int, cols: int, n_exceptions: int, x, y, batch: int = 1,

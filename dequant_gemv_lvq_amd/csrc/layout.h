@@ -39,6 +39,30 @@ inline Sections lp2_sections(size_t rows, size_t cols) {
   return s;
 }
 
+// Direct layout (no class table): 16-byte records, then scales and tails.
+inline Sections direct_sections(size_t rows, size_t cols) {
+  const size_t nb = cols / 24, tau = cols % 24;
+  Sections s;
+  s.table = 0;  // none
+  s.codes = 0;
+  s.cls = 0;
+  s.scale = align256(rows * nb * 16);
+  s.tail = s.scale + align256(rows * 2);
+  s.total = s.tail + align256(rows * tau * 2);
+  return s;
+}
+
+// Direct code word w (0..3) of a block carries coordinate pairs P = 3w + v
+// (v = 0, 1, 2), coordinates 2P and 2P + 1.  With |x| = 2h + p (p the
+// block's parity), view v is the word rotated right by 5v: bits 1-3 h of the
+// first coordinate, bit 15 its sign, bits 17-19 and 31 the second's.  p is
+// bit 0 of word 0; the other bits are zero.
+inline int direct_bit(int j, int field) {  // field 0..2: h bits, 3: sign
+  const int pair = j >> 1, half = j & 1, v = pair % 3;
+  const int b = (field < 3 ? 1 + field : 15) + 16 * half;
+  return (b + 5 * v) & 31;
+}
+
 // LP2X: the LP2 blob followed by an exception side channel for the blocks LP2
 // cannot hold (their main record is zero): row offsets u32 [rows + 1] and
 // 16-byte entries {block index | class id << 16, the three LP3 code words}.

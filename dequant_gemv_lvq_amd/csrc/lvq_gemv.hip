@@ -99,6 +99,18 @@ __host__ __device__ inline LeechView lp2_view(const void* blob, size_t rows, siz
   return v;
 }
 
+__host__ __device__ inline LeechView direct_view(const void* blob, size_t rows, size_t cols) {
+  const Sections s = direct_sections(rows, cols);
+  const uint8_t* b = (const uint8_t*)blob;
+  LeechView v;
+  v.table = nullptr;
+  v.codes = (const uint32_t*)b;
+  v.cls = nullptr;
+  v.scale = (const uint16_t*)(b + s.scale);
+  v.tail = (const uint16_t*)(b + s.tail);
+  return v;
+}
+
 __host__ __device__ inline LeechView leech_view(const void* blob, size_t rows, size_t cols) {
   const Sections s = blob_sections(rows, cols);
   const uint8_t* b = (const uint8_t*)blob;
@@ -140,7 +152,11 @@ constexpr int kMaxFused = 4;
 // block's weights are multiplied by gain[bit]
 // kLp2: one matrix in the LP2 layout (two rank planes, class in the record)
 // kRot: one matrix whose input is first rotated, (H kron Q)(S x), in LDS
-constexpr int kSingle = 0, kFused = 1, kNoWeights = 2, kGain = 3, kLp2 = 4, kRot = 5;
+// kDirect: one matrix in the table-free direct layout (|x| = 2h + parity)
+constexpr int kSingle = 0, kFused = 1, kNoWeights = 2, kGain = 3, kLp2 = 4, kRot = 5,
+              kDirect = 6;
+// 32-bit code words per block
+constexpr int words_of(int M) { return M == kDirect ? 4 : 3; }
 
 struct MatSet {
   LeechView v[kMaxFused];
@@ -197,9 +213,9 @@ __device__ __forceinline__ int start_of(const MatSet& ms, int m) {
 // are wave-uniform (scalar registers): each item's addresses are scalar buffer
 // resources plus a fixed per-lane offset, so no vector instruction is spent on
 // addressing.
-template <int BPL>
+template <int BPL, int M>
 struct ItemRegs {
-  uint32_t w[BPL][3];
+  uint32_t w[BPL][words_of(M)];
   uint32_t c[BPL];
   uint32_t tail;   // this lane's tail value (0 for lanes >= tau)
   uint32_t scale;  // the row's fp16 scale
@@ -232,14 +248,14 @@ __device__ __forceinline__ uint32_t weight_bytes(uint32_t n) {
 
 template <int BPL, int M>
 __device__ __forceinline__ void load_meta(const MatSet& ms, int nb, int tau, int gr, int chunk,
-                                          int lane, ItemRegs<BPL>& g) {
+                                          int lane, ItemRegs<BPL, M>& g) {
   const int m = mat_of<M>(ms, gr);
   const int r = gr - start_of<M>(ms, m);
   const uint16_t* cls = pick<M>(ms, m, [](const MatSet& s, int i) { return s.v[i].cls; });
   const uint16_t* tail = pick<M>(ms, m, [](const MatSet& s, int i) { return s.v[i].tail; });
   const uint16_t* scale = pick<M>(ms, m, [](const MatSet& s, int i) { return s.v[i].scale; });
   const int k0 = chunk * (kWave * BPL);
-  if (M != kLp2) {  // LP2 keeps the class inside the code record
+  if (M != kLp2 && M != kDirect) {  // LP2 keeps the class in the record; direct has none
     const auto rc =
         buffer_rsrc(cls + (size_t)r * nb + k0, weight_bytes<M>((uint32_t)(nb - k0) * 2));
 #pragma unroll
@@ -254,13 +270,29 @@ __device__ __forceinline__ void load_meta(const MatSet& ms, int nb, int tau, int
   g.scale = __builtin_amdgcn_raw_buffer_load_b16(rs, 0, 0, 0);
 }
 
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
 template <int BPL, int M>
 __device__ __forceinline__ void load_codes(const MatSet& ms, int nb, int gr, int chunk, int lane,
-                                           ItemRegs<BPL>& g) {
+                                           ItemRegs<BPL, M>& g) {
   const int m = mat_of<M>(ms, gr);
   const int r = gr - start_of<M>(ms, m);
   const uint32_t* codes = pick<M>(ms, m, [](const MatSet& s, int i) { return s.v[i].codes; });
   const int k0 = chunk * (kWave * BPL);
+  if constexpr (M == kDirect) {
+    // one 16-byte record per block
+    const auto rw = buffer_rsrc(codes + ((size_t)r * nb + k0) * 4, (uint32_t)(nb - k0) * 16);
+#pragma unroll
+    for (int u = 0; u < BPL; ++u) {
+      const auto v = __builtin_bit_cast(
+          u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rw, (lane + u * kWave) * 16, 0, kStream));
+      g.w[u][0] = v.x;
+      g.w[u][1] = v.y;
+      g.w[u][2] = v.z;
+      g.w[u][3] = v.w;
+    }
+    return;
+  } else {
   const auto rw = buffer_rsrc(codes + ((size_t)r * nb + k0) * 3,
                               weight_bytes<M>((uint32_t)(nb - k0) * 12));
 #pragma unroll
@@ -270,12 +302,13 @@ __device__ __forceinline__ void load_codes(const MatSet& ms, int nb, int gr, int
     g.w[u][1] = __builtin_amdgcn_raw_buffer_load_b32(rw, o + 4, 0, kStream);
     g.w[u][2] = __builtin_amdgcn_raw_buffer_load_b32(rw, o + 8, 0, kStream);
   }
+  }
 }
 
 // Both groups, metadata first, so a table lookup never waits for code words.
 template <int BPL, int M>
 __device__ __forceinline__ void load_item(const MatSet& ms, int nb, int tau, int gr, int chunk,
-                                          int lane, ItemRegs<BPL>& g) {
+                                          int lane, ItemRegs<BPL, M>& g) {
   load_meta<BPL, M>(ms, nb, tau, gr, chunk, lane, g);
   load_codes<BPL, M>(ms, nb, gr, chunk, lane, g);
 }
@@ -287,7 +320,7 @@ __device__ __forceinline__ void load_item(const MatSet& ms, int nb, int tau, int
 template <int B, int BPL, int M>
 __device__ __forceinline__ void decode_item(const MatSet& ms, int nb, int tau, int nchunks,
                                             int kpad, int gr, int chunk, int lane,
-                                            const ItemRegs<BPL>& g, const uint2* lut,
+                                            const ItemRegs<BPL, M>& g, const uint2* lut,
                                             const uint32_t* xs, float (&acc)[B][3]) {
   asm volatile("" ::: "memory");  // keep this item's LDS reads inside this item
   // Word wi of every block goes to accumulator wi: consecutive words always
@@ -299,6 +332,30 @@ __device__ __forceinline__ void decode_item(const MatSet& ms, int nb, int tau, i
   const uint32_t* xl = xs + (chunk * (kWave * BPL) + lane) * 12;
 #pragma unroll
   for (int u = 0; u < BPL; ++u) {
+    if constexpr (M == kDirect) {
+      // view v of word w: the word rotated right by 5v, AND the h and sign
+      // fields, OR the block parity into bit 0 of both halves: the fp16
+      // subnormal pair (2h + p) 2^-24 with its signs, no table
+      const uint32_t pp = (g.w[u][0] & 1u) * 0x00010001u;
+#pragma unroll
+      for (int bb = 0; bb < B; ++bb) {
+        const uint4* xb = (const uint4*)(xl + bb * npair + u * (kWave * 12));
+        const uint4 q0 = xb[0], q1 = xb[1], q2 = xb[2];
+        const uint32_t xp[12] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w,
+                                 q2.x, q2.y, q2.z, q2.w};
+#pragma unroll
+        for (int wi = 0; wi < 4; ++wi) {
+#pragma unroll
+          for (int vi = 0; vi < 3; ++vi) {
+            const uint32_t w = g.w[u][wi];
+            const uint32_t r = vi ? __builtin_amdgcn_alignbit(w, w, 5 * vi) : w;
+            const uint32_t d = (r & 0x800E800Eu) | pp;
+            acc[bb][vi] = dot2(d, xp[3 * wi + vi], acc[bb][vi]);
+          }
+        }
+      }
+      continue;
+    }
     // ids < 302 by construction (lvq_expand); bit 15 is the gain bit (kGain);
     // LP2: the id sits in the odd bits 9..15 and 25..31 of word 0
     const uint32_t w0 = g.w[u][0];
@@ -556,12 +613,12 @@ leech_gemv_kernel(MatSet ms, int rows, int nb, int tau, int cols, int nchunks, i
     }
   }
   const uint64_t* table = ms.v[0].table;  // the same universal table in every blob
-  const uint64_t te = table[min(tid, LVQ_NUM_CLASSES - 1)];
+  const uint64_t te = M == kDirect ? 0 : table[min(tid, LVQ_NUM_CLASSES - 1)];
   asm volatile("" ::: "memory");
   // 2. the first two items (a wave with fewer items loads rows it never
   //    uses, so that the load sequence has no branches and every later wait
   //    counts exactly)
-  ItemRegs<BPL> ia, ib;
+  ItemRegs<BPL, M> ia, ib;
   int ra = wave < rows ? wave : 0, ca = 0;
   int rb = ca + 1 == nchunks ? ra + nwaves : ra, cb = ca + 1 == nchunks ? 0 : ca + 1;
   if (items < 2) { rb = ra; cb = ca; }
@@ -569,7 +626,7 @@ leech_gemv_kernel(MatSet ms, int rows, int nb, int tau, int cols, int nchunks, i
   load_item<BPL, M>(ms, nb, tau, rb, cb, lane, ib);
   asm volatile("" ::: "memory");
   // 3. the class table into LDS; the barrier also waits for x
-  for (int c = tid; c < LVQ_NUM_CLASSES; c += nthr) {
+  for (int c = tid; M != kDirect && c < LVQ_NUM_CLASSES; c += nthr) {
     const uint64_t e = c == tid ? te : table[c];
     lut[c] = M == kLp2 ? stage_lut_lp2(e) : stage_lut(c, e);
   }
@@ -790,6 +847,7 @@ int launch_leech_bpl(const MatSet& ms, int mode, int rows, int cols, const uint1
     if (mode == kGain) return launch_leech_mode<B, BPL, kGain>(ms, rows, cols, x, st);
   }
   if (mode == kLp2) return launch_leech_mode<B, BPL, kLp2>(ms, rows, cols, x, st);
+  if (mode == kDirect) return launch_leech_mode<B, BPL, kDirect>(ms, rows, cols, x, st);
   if constexpr (gain_bpl_ok(B, BPL)) {
     if (mode == kRot) return launch_leech_mode<B, BPL, kRot>(ms, rows, cols, x, st);
   }
@@ -872,8 +930,9 @@ int single_gemv(const void* blob, int rows, int cols, const uint16_t* x, float* 
   if (rows == 0) return LVQ_OK;
   if (cols == 0) return zero_output(y, (size_t)batch * rows, st);
   MatSet ms = {};
-  ms.v[0] = mode == kLp2 ? lp2_view(blob, (size_t)rows, (size_t)cols)
-                         : leech_view(blob, (size_t)rows, (size_t)cols);
+  ms.v[0] = mode == kLp2      ? lp2_view(blob, (size_t)rows, (size_t)cols)
+            : mode == kDirect ? direct_view(blob, (size_t)rows, (size_t)cols)
+                              : leech_view(blob, (size_t)rows, (size_t)cols);
   ms.y[0] = y;
   ms.start[0] = 0;
   for (int i = 1; i <= kMaxFused; ++i) ms.start[i] = rows;
@@ -894,6 +953,11 @@ using namespace lvq;
 extern "C" int lvq_gemv(const void* blob, int rows, int cols, const uint16_t* x, float* y,
                         int batch, void* stream) {
   return single_gemv(blob, rows, cols, x, y, batch, stream, kSingle);
+}
+
+extern "C" int lvq_gemv_direct(const void* blob, int rows, int cols, const uint16_t* x, float* y,
+                               int batch, void* stream) {
+  return single_gemv(blob, rows, cols, x, y, batch, stream, kDirect);
 }
 
 extern "C" int lvq_gemv_lp2(const void* blob, int rows, int cols, const uint16_t* x, float* y,

@@ -27,6 +27,12 @@ Inside code word w, slot n (0..7) is coordinate j = 8w + 2 (n % 4) + n // 4
 (slots v and v + 4 carry two adjacent columns):
   bits 4n .. 4n+2          table slot of the coordinate: rank + 1 (1..5)
   bit (4n + 11) mod 32     1 if x_j >= 0, 0 if x_j < 0
+
+The compact LP2 / LP2X layouts and the table-free direct layout have their
+own unpackers below (sections_*, unpack_*), each read from its byte layout
+alone.  Direct layout: every coordinate of a lattice point has the block's
+parity p, so |x_j| = 2 e_j + p with e_j = 0..6 in the ball; a 16-byte record
+holds p, e_j and the sign of each coordinate, and no class table is needed.
 """
 import numpy as np
 
@@ -273,3 +279,50 @@ def unpack_lp2x(blob, rows: int, cols: int, n_exc: int) -> dict:
             assert not np.any(coords[r * nb + k]), "side-channel block with a main record"
             coords[r * nb + k] = x
     return {"coords": coords.astype(np.int8).reshape(rows, nb, 24), "exc_off": exc_off.copy()}
+
+
+def sections_direct(rows: int, cols: int) -> dict:
+    nb, tau = cols // 24, cols % 24
+    off = {}
+    pos = 0
+    for name, size in (("codes", rows * nb * 16), ("scale", rows * 2), ("tail", rows * tau * 2)):
+        off[name] = pos
+        pos += _align(size)
+    off["total"] = pos
+    return off
+
+
+def direct_bytes(rows: int, cols: int) -> int:
+    """Direct-layout weight bytes: 16 per block, 2 per row, 2 per tail column."""
+    nb, tau = cols // 24, cols % 24
+    return rows * (16 * nb + 2 + 2 * tau)
+
+
+def unpack_direct(blob, rows: int, cols: int) -> dict:
+    """Coordinates int8 [R][nb][24], scales and tails from a direct-layout
+    blob: no class table.  Each block is four little-endian 32-bit words; the
+    block parity p is bit 0 of word 0; coordinate j sits in word (j // 2) // 3
+    with view v = (j // 2) % 3 and half h = j % 2, its three magnitude bits
+    e at (1 + f + 16 h + 5 v) mod 32 and its sign at (15 + 16 h + 5 v) mod 32,
+    and |x_j| = 2 e + p."""
+    buf = np.frombuffer(bytes(blob), dtype=np.uint8)
+    off = sections_direct(rows, cols)
+    assert buf.size == off["total"], (buf.size, off["total"])
+    nb, tau = cols // 24, cols % 24
+    words = buf[off["codes"]: off["codes"] + rows * nb * 16].view("<u4").reshape(rows * nb, 4)
+    words = words.astype(np.int64)
+    p = words[:, 0] & 1
+    coords = np.zeros((rows * nb, 24), dtype=np.int64)
+    for j in range(24):
+        pair, h = divmod(j, 2)
+        w, v = divmod(pair, 3)
+        e = np.zeros(rows * nb, dtype=np.int64)
+        for f in range(3):
+            e |= ((words[:, w] >> ((1 + f + 16 * h + 5 * v) % 32)) & 1) << f
+        neg = (words[:, w] >> ((15 + 16 * h + 5 * v) % 32)) & 1
+        mag = 2 * e + p
+        coords[:, j] = np.where(neg == 1, -mag, mag)
+    return {"coords": coords.astype(np.int8).reshape(rows, nb, 24),
+            "words": words.astype(np.uint32).reshape(rows, nb, 4),
+            "scale": buf[off["scale"]: off["scale"] + rows * 2].view("<u2").copy(),
+            "tail": buf[off["tail"]: off["tail"] + rows * tau * 2].view("<u2").reshape(rows, tau).copy()}

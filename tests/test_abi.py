@@ -392,3 +392,78 @@ def test_gemv_rotated_validates_before_launch():
     assert g(A, 4, 3 * 1024, None, A + 8, 3, A, A, 1, None) == lvq.LVQ_E_ALIGN
     assert g(A, 4, 4096, None, None, 1, A, A, 0, None) == lvq.LVQ_E_BATCH
     assert g(A, 0, 4096, None, None, 1, A, A, 1, None) == lvq.LVQ_OK
+
+
+def _direct_words(x):
+    blob = lvq.expand_direct(np.asarray(x, np.int8).reshape(1, 1, 24), synth.fp16_bits([1.0]),
+                             None, 1, 24)
+    return [int(w) for w in blob[:16].view("<u4")]
+
+
+def test_expand_direct_hand_records():
+    # records worked out by hand from the layout rule (|x| = 2e + p; pair P =
+    # j // 2 in word P // 3, view v = P % 3, half h = j % 2; e bit f at
+    # 1 + f + 16h + 5v, sign at 15 + 16h + 5v, both mod 32)
+    x = [4, 4] + [0] * 22                      # e = 2 at j = 0, 1: bits 2 and 18
+    assert _direct_words(x) == [0x00040004, 0, 0, 0]
+    x = [-3] + [1] * 23                        # p = 1; e = 1 at j = 0, sign bit 15
+    assert _direct_words(x) == [0x8003, 0, 0, 0]
+    x = [1] * 23 + [-3]                        # j = 23: word 3, v = 2, h = 1
+    assert _direct_words(x) == [1, 0, 0, (1 << 27) | (1 << 9)]
+    x = [1] * 23 + [13]                        # e = 6: bits 28, 29 (shell 12)
+    assert _direct_words(x) == [1, 0, 0, 0x30000000]
+    for x in ([4, 4] + [0] * 22, [-3] + [1] * 23, [1] * 23 + [-3], [1] * 23 + [13]):
+        assert leech.is_leech(np.array(x))
+        blob = lvq.expand_direct(np.array(x, np.int8).reshape(1, 1, 24), synth.fp16_bits([1.0]),
+                                 None, 1, 24)
+        assert list(layout.unpack_direct(blob, 1, 24)["coords"].reshape(24)) == x
+
+
+@pytest.mark.parametrize("src", ["ball", "all_classes", "tail_only"])
+def test_expand_direct_round_trips_through_the_oracle_unpacker(src):
+    if src == "ball":
+        rows, cols = 40, 24 * 200 + 7
+        d = synth.leech_matrix(rows, cols, 6, key=(41,))
+        coords, scale, tail = d["coords"], d["scale"], d["tail"]
+    elif src == "all_classes":
+        rows, nb = 30, 50
+        cols = 24 * nb
+        coords, _ = _all_class_coords(rows, nb, 4)
+        scale, tail = synth.fp16_bits(np.ones(rows)), None
+    else:
+        rows, cols = 3, 11
+        coords = np.zeros((3, 0, 24), np.int8)
+        scale, tail = synth.fp16_bits(np.ones(rows)), synth.fp16_bits(np.ones((rows, 11)))
+    blob = lvq.expand_direct(coords, scale, tail, rows, cols)
+    assert blob.size == lvq.layout_bytes_direct(rows, cols) == layout.sections_direct(rows, cols)["total"]
+    u = layout.unpack_direct(blob, rows, cols)
+    assert np.array_equal(u["coords"], coords)
+    assert np.array_equal(u["scale"], scale)
+    if tail is not None:
+        assert np.array_equal(u["tail"], tail)
+    # the bits outside p, e and the signs are zero
+    used = 1
+    for v in range(3):
+        for h in range(2):
+            for b in (1, 2, 3, 15):
+                used |= 1 << ((b + 16 * h + 5 * v) % 32)
+    w = u["words"].reshape(-1, 4).astype(np.int64)
+    assert np.all(w[:, 0] & ~used & 0xFFFFFFFF == 0)
+    assert np.all(w[:, 1:] & ~(used & ~1) & 0xFFFFFFFF == 0)
+
+
+def test_expand_direct_refusals_and_validation():
+    x = np.zeros((2, 3, 24), dtype=np.int8)
+    x[1, 2, 0] = 1  # not a lattice point
+    with pytest.raises(lvq.LvqError) as e:
+        lvq.expand_direct(x, synth.fp16_bits(np.ones(2)), None, 2, 72)
+    assert e.value.code == lvq.LVQ_E_NOT_LEECH and e.value.index == (1, 2)
+    lib = lvq.library()
+    A = 1 << 20
+    g = lib.lvq_gemv_direct
+    assert g(None, 4, 48, A, A, 1, None) == lvq.LVQ_E_NULL
+    assert g(A + 4, 4, 48, A, A, 1, None) == lvq.LVQ_E_ALIGN
+    assert g(A, 4, 48, A, A, 0, None) == lvq.LVQ_E_BATCH
+    assert g(A, 4, 48, A, A, 5, None) == lvq.LVQ_E_BATCH
+    assert g(A, -1, 48, A, A, 1, None) == lvq.LVQ_E_SHAPE
+    assert g(A, 0, 48, A, A, 1, None) == lvq.LVQ_OK
