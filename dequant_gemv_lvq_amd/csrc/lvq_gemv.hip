@@ -246,6 +246,18 @@ __device__ __forceinline__ uint32_t weight_bytes(uint32_t n) {
   return M == kNoWeights ? 0u : n;
 }
 
+// A lane's byte offset, opaque to the optimiser for this item.  Without it
+// the offsets of the item's loads (lane * size + u * 64 * size + 4 k) are loop
+// invariants, hoisted into one register each: a register per load, and loads
+// the backend can no longer merge (three dword loads per block instead of one
+// dwordx3).  Computed afresh per item, the constants fold into the loads'
+// immediate offsets and every load of the item shares one address register.
+__device__ __forceinline__ int lane_offset(int lane, int size) {
+  int o = lane * size;
+  asm volatile("" : "+v"(o));
+  return o;
+}
+
 template <int BPL, int M>
 __device__ __forceinline__ void load_meta(const MatSet& ms, int nb, int tau, int gr, int chunk,
                                           int lane, ItemRegs<BPL, M>& g) {
@@ -258,9 +270,10 @@ __device__ __forceinline__ void load_meta(const MatSet& ms, int nb, int tau, int
   if (M != kLp2 && M != kDirect) {  // LP2 keeps the class in the record; direct has none
     const auto rc =
         buffer_rsrc(cls + (size_t)r * nb + k0, weight_bytes<M>((uint32_t)(nb - k0) * 2));
+    const int lo = lane_offset(lane, 2);
 #pragma unroll
     for (int u = 0; u < BPL; ++u)
-      g.c[u] = __builtin_amdgcn_raw_buffer_load_b16(rc, (lane + u * kWave) * 2, 0, kStream);
+      g.c[u] = __builtin_amdgcn_raw_buffer_load_b16(rc, lo + u * (kWave * 2), 0, kStream);
   }
   const auto rt = buffer_rsrc(tail + (size_t)r * tau, weight_bytes<M>((uint32_t)tau * 2));
   g.tail = __builtin_amdgcn_raw_buffer_load_b16(rt, lane * 2, 0, 0);
@@ -282,10 +295,11 @@ __device__ __forceinline__ void load_codes(const MatSet& ms, int nb, int gr, int
   if constexpr (M == kDirect) {
     // one 16-byte record per block
     const auto rw = buffer_rsrc(codes + ((size_t)r * nb + k0) * 4, (uint32_t)(nb - k0) * 16);
+    const int lo = lane_offset(lane, 16);
 #pragma unroll
     for (int u = 0; u < BPL; ++u) {
       const auto v = __builtin_bit_cast(
-          u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rw, (lane + u * kWave) * 16, 0, kStream));
+          u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rw, lo + u * (kWave * 16), 0, kStream));
       g.w[u][0] = v.x;
       g.w[u][1] = v.y;
       g.w[u][2] = v.z;
@@ -295,9 +309,10 @@ __device__ __forceinline__ void load_codes(const MatSet& ms, int nb, int gr, int
   } else {
   const auto rw = buffer_rsrc(codes + ((size_t)r * nb + k0) * 3,
                               weight_bytes<M>((uint32_t)(nb - k0) * 12));
+  const int lo = lane_offset(lane, 12);
 #pragma unroll
   for (int u = 0; u < BPL; ++u) {
-    const int o = (lane + u * kWave) * 12;
+    const int o = lo + u * (kWave * 12);
     g.w[u][0] = __builtin_amdgcn_raw_buffer_load_b32(rw, o, 0, kStream);
     g.w[u][1] = __builtin_amdgcn_raw_buffer_load_b32(rw, o + 4, 0, kStream);
     g.w[u][2] = __builtin_amdgcn_raw_buffer_load_b32(rw, o + 8, 0, kStream);
