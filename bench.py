@@ -209,6 +209,13 @@ def direct_bytes(rows, cols):
     return rows * (16 * nb + 2 + 2 * tau)
 
 
+def onehot_bytes(rows, cols):
+    """One-hot layout: 16 B of rank-indicator masks and signs plus a 2 B class
+    id per 24-weight block, 2 B per row for the scale, 2 B per tail column."""
+    nb, tau = cols // 24, cols % 24
+    return rows * (18 * nb + 2 + 2 * tau)
+
+
 def bpdq_bytes(rows, cols):
     return (cols // 16) * rows * 4 + (cols // 256) * 3 * rows * 2
 
@@ -422,20 +429,29 @@ class Bench:
 
     def leech_direct(self, cfg, rows, cols, batch, d=None):
         """The table-free direct layout (|x| = 2e + parity) at one shape."""
+        return self._layout("leech_direct", self.lvq.expand_direct, self.lvq.gemv_direct,
+                            direct_bytes, cfg, rows, cols, batch, d)
+
+    def leech_onehot(self, cfg, rows, cols, batch, d=None):
+        """The one-hot layout (rank-indicator masks) at one shape."""
+        return self._layout("leech_onehot", self.lvq.expand_onehot, self.lvq.gemv_onehot,
+                            onehot_bytes, cfg, rows, cols, batch, d)
+
+    def _layout(self, arm, expand, gemv, nbytes, cfg, rows, cols, batch, d):
         import synth
-        torch, lvq = self.torch, self.lvq
+        torch = self.torch
         if d is None:
             d = synth.leech_matrix(rows, cols, cfg)
-        blob = lvq.expand_direct(d["coords"], d["scale"], d["tail"], rows, cols)
+        blob = expand(d["coords"], d["scale"], d["tail"], rows, cols)
         x = synth.activations(cols, batch, cfg, rows=rows)
         n = copies_for(blob.size)
         bufs = dev_copies(torch, blob, n)
         xd = to_dev(torch, x)
         yd = torch.empty((batch, rows), dtype=torch.float32, device="cuda")
-        tm = self.time(lambda i: lvq.gemv_direct(bufs[i % n], rows, cols, xd, yd, batch))
+        tm = self.time(lambda i: gemv(bufs[i % n], rows, cols, xd, yd, batch))
         del bufs
         torch.cuda.empty_cache()
-        return self.record("leech_direct", cfg, rows, cols, batch, direct_bytes(rows, cols), n, tm,
+        return self.record(arm, cfg, rows, cols, batch, nbytes(rows, cols), n, tm,
                            blob_bytes=int(blob.size))
 
     def leech_lp2x(self, cfg, rows, cols, batch, d=None):
@@ -824,6 +840,8 @@ def main():
         records.append(B.leech_direct(4, ROWS, COLS, 1, d=d))
         records.append(B.leech_direct(4, ROWS, COLS, 4, d=d))
         records.append(B.leech_direct(3, 12288, 4096, 1))
+        records.append(B.leech_onehot(4, ROWS, COLS, 1, d=d))
+        records.append(B.leech_onehot(3, 12288, 4096, 1))
         records.append(B.unfold(ROWS * (COLS // 24)))
         fp16_by_shape = {(r["R"], r["K"]): r["gbps"] for r in records if r["arm"] == "fp16"}
         for r in records:

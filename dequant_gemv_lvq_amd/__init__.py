@@ -69,6 +69,9 @@ def _load():
         "lvq_layout_bytes_direct": (sz, [i, i]),
         "lvq_expand_direct": (i, [vp, vp, vp, i, i, vp]),
         "lvq_gemv_direct": (i, [vp, i, i, vp, vp, i, vp]),
+        "lvq_layout_bytes_onehot": (sz, [i, i]),
+        "lvq_expand_onehot": (i, [vp, vp, vp, i, i, vp]),
+        "lvq_gemv_onehot": (i, [vp, i, i, vp, vp, i, vp]),
         "lvq_rank": (i, [vp, sz, vp]),
         "lvq_unfold": (i, [vp, sz, vp, vp, vp]),
         "lvq_gemv_gain": (i, [vp, i, i, ctypes.c_float, ctypes.c_float, vp, vp, i, vp]),
@@ -95,6 +98,7 @@ EXPORTED = ("lvq_strerror", "lvq_last_error_index", "lvq_class_table", "lvq_layo
             "lvq_expand", "lvq_expand_gain", "lvq_layout_bytes_lp2", "lvq_expand_lp2",
             "lvq_gemv_lp2", "lvq_lp2x_exceptions", "lvq_layout_bytes_lp2x", "lvq_expand_lp2x",
             "lvq_gemv_lp2x", "lvq_layout_bytes_direct", "lvq_expand_direct", "lvq_gemv_direct",
+            "lvq_layout_bytes_onehot", "lvq_expand_onehot", "lvq_gemv_onehot",
             "lvq_rank", "lvq_gemv", "lvq_gemv_gain",
             "lvq_unfold", "lvq_gemv_fused", "lvq_gemv_noweights", "lvq_decode",
             "bpdq_gemv", "trellis_gemv", "fp16_gemv", "lvq_rotate", "lvq_gemv_rotated",
@@ -204,17 +208,31 @@ def layout_bytes_direct(rows: int, cols: int) -> int:
     return int(_lib.lvq_layout_bytes_direct(int(rows), int(cols)))
 
 
+def layout_bytes_onehot(rows: int, cols: int) -> int:
+    return int(_lib.lvq_layout_bytes_onehot(int(rows), int(cols)))
+
+
+def expand_onehot(coords, scale, tail, rows: int, cols: int) -> np.ndarray:
+    """Host expansion into the one-hot layout (rank-indicator masks)."""
+    return _expand_with(_lib.lvq_expand_onehot, _lib.lvq_layout_bytes_onehot, coords, scale,
+                        tail, rows, cols)
+
+
 def expand_direct(coords, scale, tail, rows: int, cols: int) -> np.ndarray:
     """Host expansion into the direct layout (|x| = 2e + parity, no table)."""
+    return _expand_with(_lib.lvq_expand_direct, _lib.lvq_layout_bytes_direct, coords, scale,
+                        tail, rows, cols)
+
+
+def _expand_with(expand, nbytes, coords, scale, tail, rows: int, cols: int) -> np.ndarray:
     coords = np.ascontiguousarray(coords, dtype=np.int8)
     scale = np.ascontiguousarray(scale, dtype=np.uint16)
     tau = cols % 24
     tail = None if tau == 0 else np.ascontiguousarray(tail, dtype=np.uint16)
     if rows < 0 or cols < 0 or coords.size != rows * (cols // 24) * 24:
         _check(LVQ_E_SHAPE)
-    blob = np.empty(_lib.lvq_layout_bytes_direct(int(rows), int(cols)), dtype=np.uint8)
-    code = _lib.lvq_expand_direct(_ptr(coords), _ptr(scale), _ptr(tail), int(rows), int(cols),
-                                  blob.ctypes.data)
+    blob = np.empty(nbytes(int(rows), int(cols)), dtype=np.uint8)
+    code = expand(_ptr(coords), _ptr(scale), _ptr(tail), int(rows), int(cols), blob.ctypes.data)
     if code != LVQ_OK:
         r, b = ctypes.c_int(), ctypes.c_int()
         _lib.lvq_last_error_index(ctypes.byref(r), ctypes.byref(b))
@@ -306,6 +324,11 @@ def gemv_noweights(blob, rows: int, cols: int, x, y, batch: int = 1, stream=None
 def gemv_lp2(blob, rows: int, cols: int, x, y, batch: int = 1, stream=None):
     _check(_lib.lvq_gemv_lp2(_ptr(blob), int(rows), int(cols), _ptr(x), _ptr(y), int(batch),
                              _stream(stream)))
+
+
+def gemv_onehot(blob, rows: int, cols: int, x, y, batch: int = 1, stream=None):
+    _check(_lib.lvq_gemv_onehot(_ptr(blob), int(rows), int(cols), _ptr(x), _ptr(y), int(batch),
+                                _stream(stream)))
 
 
 def gemv_direct(blob, rows: int, cols: int, x, y, batch: int = 1, stream=None):

@@ -335,6 +335,50 @@ int lvq_expand_direct(const int8_t* coords, const uint16_t* scale, const uint16_
   return LVQ_OK;
 }
 
+size_t lvq_layout_bytes_onehot(int rows, int cols) {
+  if (rows < 0 || cols < 0) return 0;
+  return lvq::onehot_sections((size_t)rows, (size_t)cols).total;
+}
+
+int lvq_expand_onehot(const int8_t* coords, const uint16_t* scale, const uint16_t* tail, int rows,
+                      int cols, void* blob_out) {
+  g_err_row = g_err_block = -1;
+  if (rows < 0 || cols < 0) return LVQ_E_SHAPE;
+  const size_t R = (size_t)rows, nb = (size_t)cols / 24, tau = (size_t)cols % 24;
+  if (!blob_out || (R && !scale) || (R && nb && !coords) || (R && tau && !tail))
+    return LVQ_E_NULL;
+  const lvq::Sections s = lvq::onehot_sections(R, (size_t)cols);
+  uint8_t* out = (uint8_t*)blob_out;
+  std::memset(out, 0, s.total);
+  const ClassTable& T = table();
+  std::memcpy(out + s.table, T.entries.data(), LVQ_NUM_CLASSES * 8);
+  uint32_t* codes = (uint32_t*)(out + s.codes);
+  uint16_t* cls = (uint16_t*)(out + s.cls);
+  for (size_t b = 0; b < R * nb; ++b) {
+    const int8_t* x = coords + b * 24;
+    int id = 0;
+    const int err = classify(x, &id);  // membership and the norm limit
+    if (err) {
+      g_err_row = (int)(b / nb);
+      g_err_block = (int)(b % nb);
+      return err;
+    }
+    const ClassInfo& c = T.cls[id];
+    uint32_t w[4] = {0, 0, 0, 0};
+    for (int j = 0; j < 24; ++j) {
+      const int a = x[j] < 0 ? -x[j] : x[j];
+      const int rank = c.slot_of_mag[a] - 1;  // 0..4
+      if (rank > 0) w[rank - 1] |= 1u << lvq::onehot_mask_bit(j);
+      if (x[j] < 0) w[lvq::onehot_sign_word(j)] |= 1u << lvq::onehot_sign_bit(j);
+    }
+    std::memcpy(codes + b * 4, w, 16);
+    cls[b] = (uint16_t)id;
+  }
+  if (R) std::memcpy(out + s.scale, scale, R * 2);
+  if (R && tau) std::memcpy(out + s.tail, tail, R * tau * 2);
+  return LVQ_OK;
+}
+
 int lvq_expand_lp2x(const int8_t* coords, const uint16_t* scale, const uint16_t* tail, int rows,
                     int cols, size_t n_exceptions, void* blob_out) {
   return expand_impl(coords, nullptr, scale, tail, rows, cols, blob_out, kLp2x, n_exceptions);

@@ -63,6 +63,26 @@ inline int direct_bit(int j, int field) {  // field 0..2: h bits, 3: sign
   return (b + 5 * v) & 31;
 }
 
+// One-hot blob: the LP3 sections with 16-byte code records (four words).
+// Word i (0..3) is the indicator mask of rank i + 1 (rank 0: no bit set):
+// coordinate 2P at bit P, coordinate 2P + 1 at bit 16 + P (P = 0..11).  Its
+// spare bits 12-14 and 28-30 carry the signs of pairs 3i .. 3i + 2 (bit
+// 12 + P - 3i for coordinate 2P, 28 + P - 3i for 2P + 1; 1 = negative).
+inline Sections onehot_sections(size_t rows, size_t cols) {
+  const size_t nb = cols / 24, tau = cols % 24;
+  Sections s;
+  s.table = 0;
+  s.codes = s.table + align256((size_t)LVQ_NUM_CLASSES * 8);
+  s.cls = s.codes + align256(rows * nb * 16);
+  s.scale = s.cls + align256(rows * nb * 2);
+  s.tail = s.scale + align256(rows * 2);
+  s.total = s.tail + align256(rows * tau * 2);
+  return s;
+}
+inline int onehot_mask_bit(int j) { return (j >> 1) + 16 * (j & 1); }
+inline int onehot_sign_word(int j) { return (j >> 1) / 3; }
+inline int onehot_sign_bit(int j) { return 12 + (j >> 1) % 3 + 16 * (j & 1); }
+
 // LP2X: the LP2 blob followed by an exception side channel for the blocks LP2
 // cannot hold (their main record is zero): row offsets u32 [rows + 1] and
 // 16-byte entries {block index | class id << 16, the three LP3 code words}.

@@ -111,6 +111,18 @@ __host__ __device__ inline LeechView direct_view(const void* blob, size_t rows, 
   return v;
 }
 
+__host__ __device__ inline LeechView onehot_view(const void* blob, size_t rows, size_t cols) {
+  const Sections s = onehot_sections(rows, cols);
+  const uint8_t* b = (const uint8_t*)blob;
+  LeechView v;
+  v.table = (const uint64_t*)(b + s.table);
+  v.codes = (const uint32_t*)(b + s.codes);
+  v.cls = (const uint16_t*)(b + s.cls);
+  v.scale = (const uint16_t*)(b + s.scale);
+  v.tail = (const uint16_t*)(b + s.tail);
+  return v;
+}
+
 __host__ __device__ inline LeechView leech_view(const void* blob, size_t rows, size_t cols) {
   const Sections s = blob_sections(rows, cols);
   const uint8_t* b = (const uint8_t*)blob;
@@ -153,10 +165,11 @@ constexpr int kMaxFused = 4;
 // kLp2: one matrix in the LP2 layout (two rank planes, class in the record)
 // kRot: one matrix whose input is first rotated, (H kron Q)(S x), in LDS
 // kDirect: one matrix in the table-free direct layout (|x| = 2h + parity)
+// kOneHot: one matrix in the one-hot layout (rank-indicator masks)
 constexpr int kSingle = 0, kFused = 1, kNoWeights = 2, kGain = 3, kLp2 = 4, kRot = 5,
-              kDirect = 6;
+              kDirect = 6, kOneHot = 7;
 // 32-bit code words per block
-constexpr int words_of(int M) { return M == kDirect ? 4 : 3; }
+constexpr int words_of(int M) { return M == kDirect || M == kOneHot ? 4 : 3; }
 
 struct MatSet {
   LeechView v[kMaxFused];
@@ -292,7 +305,7 @@ __device__ __forceinline__ void load_codes(const MatSet& ms, int nb, int gr, int
   const int r = gr - start_of<M>(ms, m);
   const uint32_t* codes = pick<M>(ms, m, [](const MatSet& s, int i) { return s.v[i].codes; });
   const int k0 = chunk * (kWave * BPL);
-  if constexpr (M == kDirect) {
+  if constexpr (M == kDirect || M == kOneHot) {
     // one 16-byte record per block
     const auto rw = buffer_rsrc(codes + ((size_t)r * nb + k0) * 4, (uint32_t)(nb - k0) * 16);
     const int lo = lane_offset(lane, 16);
@@ -371,6 +384,32 @@ __device__ __forceinline__ void decode_item(const MatSet& ms, int nb, int tau, i
       }
       continue;
     }
+    if constexpr (M == kOneHot) {
+      // pair P: magnitudes = m0 + sum over ranks i of [indicator] * (m_i - m0),
+      // both halves at once (indicator bits at P and 16 + P); then the two
+      // signs from the spare bits of word P / 3
+      const uint2 l = lut[g.c[u]];
+      uint32_t dm[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dm[i] = (l.y >> (8 * i)) & 0xFFu;
+#pragma unroll
+      for (int bb = 0; bb < B; ++bb) {
+        const uint4* xb = (const uint4*)(xl + bb * npair + u * (kWave * 12));
+        const uint4 q0 = xb[0], q1 = xb[1], q2 = xb[2];
+        const uint32_t xp[12] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w,
+                                 q2.x, q2.y, q2.z, q2.w};
+#pragma unroll
+        for (int P = 0; P < 12; ++P) {
+          uint32_t m = l.x;
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            m += ((g.w[u][i] >> P) & 0x00010001u) * dm[i];  // v_mad_u32_u24
+          const uint32_t d = ((g.w[u][P / 3] << (3 - P % 3)) & 0x80008000u) | m;
+          acc[bb][P % 3] = dot2(d, xp[P], acc[bb][P % 3]);
+        }
+      }
+      continue;
+    }
     // ids < 302 by construction (lvq_expand); bit 15 is the gain bit (kGain);
     // LP2: the id sits in the odd bits 9..15 and 25..31 of word 0
     const uint32_t w0 = g.w[u][0];
@@ -431,6 +470,19 @@ __device__ __forceinline__ void decode_item(const MatSet& ms, int nb, int tau, i
 // The class table staged as per-class byte LUTs (leech_lut); class 0 gets
 // 0x00 in byte 0 so that an all-zero code word reads as +0 (valid class-0
 // code words never select byte 0).
+// One-hot LUT: m0 in both 16-bit halves, and the steps m_i - m0 of ranks
+// 1..4 as bytes (0 past the class's distinct magnitudes).
+__device__ __forceinline__ uint2 stage_lut_onehot(uint64_t entry) {
+  const uint32_t m0 = (uint32_t)entry & 0xFFu;
+  uint32_t steps = 0;
+#pragma unroll
+  for (int i = 1; i <= 4; ++i) {
+    const uint32_t mi = (uint32_t)(entry >> (8 * i)) & 0xFFu;
+    steps |= (mi ? mi - m0 : 0u) << (8 * (i - 1));
+  }
+  return make_uint2(m0 * 0x00010001u, steps);
+}
+
 __device__ __forceinline__ uint2 stage_lut(int c, uint64_t entry) {
   uint2 l = leech_lut(entry);
   if (c == 0) l.x &= ~0xFFu;
@@ -441,10 +493,11 @@ __device__ __forceinline__ uint2 stage_lut(int c, uint64_t entry) {
 // VGPRs, two 1024-thread workgroups per CU) for the variants that fit there
 // without spilling, and whatever the allocation gives for the larger ones.
 // (The shape-gain mode keeps a partial sum per word and goes without, as do
-// the rotating mode, whose prologue holds 16-value butterfly sets, and LP2
-// above batch 1, whose class extraction needs the registers.)
+// the rotating mode, whose prologue holds 16-value butterfly sets, LP2
+// above batch 1, whose class extraction needs the registers, and the one-hot
+// mode, which keeps a block's four masks and its steps live across 12 pairs.)
 constexpr int leech_min_waves(int B, int BPL, int M) {
-  return M != kGain && M != kRot && !(M == kLp2 && B > 1) && B + BPL <= 4 ? 8 : 1;
+  return M != kGain && M != kRot && M != kOneHot && !(M == kLp2 && B > 1) && B + BPL <= 4 ? 8 : 1;
 }
 
 // Stages s .. s + R - 1 of every sequence of the f32 buffer fb (the m
@@ -643,7 +696,7 @@ leech_gemv_kernel(MatSet ms, int rows, int nb, int tau, int cols, int nchunks, i
   // 3. the class table into LDS; the barrier also waits for x
   for (int c = tid; M != kDirect && c < LVQ_NUM_CLASSES; c += nthr) {
     const uint64_t e = c == tid ? te : table[c];
-    lut[c] = M == kLp2 ? stage_lut_lp2(e) : stage_lut(c, e);
+    lut[c] = M == kLp2 ? stage_lut_lp2(e) : M == kOneHot ? stage_lut_onehot(e) : stage_lut(c, e);
   }
   __syncthreads();
   if (M == kRot) {
@@ -863,6 +916,7 @@ int launch_leech_bpl(const MatSet& ms, int mode, int rows, int cols, const uint1
   }
   if (mode == kLp2) return launch_leech_mode<B, BPL, kLp2>(ms, rows, cols, x, st);
   if (mode == kDirect) return launch_leech_mode<B, BPL, kDirect>(ms, rows, cols, x, st);
+  if (mode == kOneHot) return launch_leech_mode<B, BPL, kOneHot>(ms, rows, cols, x, st);
   if constexpr (gain_bpl_ok(B, BPL)) {
     if (mode == kRot) return launch_leech_mode<B, BPL, kRot>(ms, rows, cols, x, st);
   }
@@ -947,6 +1001,7 @@ int single_gemv(const void* blob, int rows, int cols, const uint16_t* x, float* 
   MatSet ms = {};
   ms.v[0] = mode == kLp2      ? lp2_view(blob, (size_t)rows, (size_t)cols)
             : mode == kDirect ? direct_view(blob, (size_t)rows, (size_t)cols)
+            : mode == kOneHot ? onehot_view(blob, (size_t)rows, (size_t)cols)
                               : leech_view(blob, (size_t)rows, (size_t)cols);
   ms.y[0] = y;
   ms.start[0] = 0;
@@ -973,6 +1028,11 @@ extern "C" int lvq_gemv(const void* blob, int rows, int cols, const uint16_t* x,
 extern "C" int lvq_gemv_direct(const void* blob, int rows, int cols, const uint16_t* x, float* y,
                                int batch, void* stream) {
   return single_gemv(blob, rows, cols, x, y, batch, stream, kDirect);
+}
+
+extern "C" int lvq_gemv_onehot(const void* blob, int rows, int cols, const uint16_t* x, float* y,
+                               int batch, void* stream) {
+  return single_gemv(blob, rows, cols, x, y, batch, stream, kOneHot);
 }
 
 extern "C" int lvq_gemv_lp2(const void* blob, int rows, int cols, const uint16_t* x, float* y,

@@ -28,9 +28,9 @@ Inside code word w, slot n (0..7) is coordinate j = 8w + 2 (n % 4) + n // 4
   bits 4n .. 4n+2          table slot of the coordinate: rank + 1 (1..5)
   bit (4n + 11) mod 32     1 if x_j >= 0, 0 if x_j < 0
 
-The compact LP2 / LP2X layouts and the table-free direct layout have their
-own unpackers below (sections_*, unpack_*), each read from its byte layout
-alone.  Direct layout: every coordinate of a lattice point has the block's
+The compact LP2 / LP2X layouts, the table-free direct layout and the
+one-hot layout (rank-indicator masks) have their own unpackers below
+(sections_*, unpack_*), each read from its byte layout alone.  Direct layout: every coordinate of a lattice point has the block's
 parity p, so |x_j| = 2 e_j + p with e_j = 0..6 in the ball; a 16-byte record
 holds p, e_j and the sign of each coordinate, and no class table is needed.
 """
@@ -324,5 +324,64 @@ def unpack_direct(blob, rows: int, cols: int) -> dict:
         coords[:, j] = np.where(neg == 1, -mag, mag)
     return {"coords": coords.astype(np.int8).reshape(rows, nb, 24),
             "words": words.astype(np.uint32).reshape(rows, nb, 4),
+            "scale": buf[off["scale"]: off["scale"] + rows * 2].view("<u2").copy(),
+            "tail": buf[off["tail"]: off["tail"] + rows * tau * 2].view("<u2").reshape(rows, tau).copy()}
+
+
+def sections_onehot(rows: int, cols: int) -> dict:
+    nb, tau = cols // 24, cols % 24
+    off = {}
+    pos = 0
+    for name, size in (("table", TABLE_ENTRIES * 8), ("codes", rows * nb * 16),
+                       ("cls", rows * nb * 2), ("scale", rows * 2), ("tail", rows * tau * 2)):
+        off[name] = pos
+        pos += _align(size)
+    off["total"] = pos
+    return off
+
+
+def onehot_bytes(rows: int, cols: int) -> int:
+    """One-hot weight bytes: 16 per block record, 2 per class id, 2 per row,
+    2 per tail column."""
+    nb, tau = cols // 24, cols % 24
+    return rows * (18 * nb + 2 + 2 * tau)
+
+
+def unpack_onehot(blob, rows: int, cols: int) -> dict:
+    """Coordinates int8 [R][nb][24], class ids, scales and tails from a
+    one-hot blob, read from the byte layout and the oracle's class table.
+    Word i of a block marks the coordinates of rank i + 1 (coordinate 2P at
+    bit P, 2P + 1 at bit 16 + P); a coordinate with no mark has rank 0; the
+    signs of pairs 3i .. 3i + 2 sit at bits 12 + P - 3i and 28 + P - 3i of
+    word i.  A coordinate marked twice is an error (the masks are one-hot)."""
+    buf = np.frombuffer(bytes(blob), dtype=np.uint8)
+    off = sections_onehot(rows, cols)
+    assert buf.size == off["total"], (buf.size, off["total"])
+    nb, tau = cols // 24, cols % 24
+    n = rows * nb
+    words = buf[off["codes"]: off["codes"] + n * 16].view("<u4").reshape(n, 4).astype(np.int64)
+    cls = buf[off["cls"]: off["cls"] + n * 2].view("<u2").astype(np.int64)
+    classes = leech.classes()
+    mags = np.zeros((len(classes), 5), dtype=np.int64)
+    for cid, c in enumerate(classes):
+        dm = sorted(set(c["key"]))
+        mags[cid, : len(dm)] = dm
+    coords = np.zeros((n, 24), dtype=np.int64)
+    for j in range(24):
+        pair, h = divmod(j, 2)
+        rank = np.zeros(n, dtype=np.int64)
+        marks = np.zeros(n, dtype=np.int64)
+        for i in range(4):
+            bit = (words[:, i] >> (pair + 16 * h)) & 1
+            rank += bit * (i + 1)
+            marks += bit
+        assert np.all(marks <= 1), "a coordinate marked by two rank masks"
+        sw = pair // 3
+        neg = (words[:, sw] >> (12 + pair - 3 * sw + 16 * h)) & 1
+        mag = mags[cls, rank]
+        coords[:, j] = np.where(neg == 1, -mag, mag)
+    return {"coords": coords.astype(np.int8).reshape(rows, nb, 24), "cls": cls.reshape(rows, nb),
+            "words": words.astype(np.uint32).reshape(rows, nb, 4),
+            "table": buf[off["table"]: off["table"] + TABLE_ENTRIES * 8].view("<u8").copy(),
             "scale": buf[off["scale"]: off["scale"] + rows * 2].view("<u2").copy(),
             "tail": buf[off["tail"]: off["tail"] + rows * tau * 2].view("<u2").reshape(rows, tau).copy()}

@@ -467,3 +467,73 @@ def test_expand_direct_refusals_and_validation():
     assert g(A, 4, 48, A, A, 5, None) == lvq.LVQ_E_BATCH
     assert g(A, -1, 48, A, A, 1, None) == lvq.LVQ_E_SHAPE
     assert g(A, 0, 48, A, A, 1, None) == lvq.LVQ_OK
+
+
+def _onehot_words(x):
+    blob = lvq.expand_onehot(np.asarray(x, np.int8).reshape(1, 1, 24), synth.fp16_bits([1.0]),
+                             None, 1, 24)
+    off = layout.sections_onehot(1, 24)["codes"]
+    return [int(w) for w in blob[off: off + 16].view("<u4")]
+
+
+def test_expand_onehot_hand_records():
+    # worked out by hand from the layout rule: word i marks rank i + 1
+    # (coordinate 2P at bit P, 2P + 1 at bit 16 + P); the sign of coordinate
+    # 2P (2P + 1) sits in word P // 3 at bit 12 + P % 3 (28 + P % 3)
+    cases = [
+        ([4, 4] + [0] * 22, [0x00010001, 0, 0, 0]),            # {0, 4}: both rank 1
+        ([-3] + [1] * 23, [0x00001001, 0, 0, 0]),               # {1, 3}: rank 1, negative
+        ([1] * 23 + [-3], [1 << 27, 0, 0, 1 << 30]),            # pair 11, odd half
+        ([1] * 23 + [13], [1 << 27, 0, 0, 0]),                  # shell 12
+        ([-3, -7] + [1] * 22, [1 | 1 << 12 | 1 << 28, 1 << 16, 0, 0]),  # {1, 3, 7}
+    ]
+    for x, want in cases:
+        assert leech.is_leech(np.array(x)), x
+        assert _onehot_words(x) == want, x
+        blob = lvq.expand_onehot(np.array(x, np.int8).reshape(1, 1, 24), synth.fp16_bits([1.0]),
+                                 None, 1, 24)
+        u = layout.unpack_onehot(blob, 1, 24)
+        assert list(u["coords"].reshape(24)) == x
+        assert int(u["cls"][0, 0]) == leech.class_of(np.array(x))
+
+
+@pytest.mark.parametrize("src", ["ball", "all_classes", "tail_only"])
+def test_expand_onehot_round_trips_through_the_oracle_unpacker(src):
+    if src == "ball":
+        rows, cols = 40, 24 * 200 + 7
+        d = synth.leech_matrix(rows, cols, 6, key=(43,))
+        coords, scale, tail = d["coords"], d["scale"], d["tail"]
+    elif src == "all_classes":
+        rows, nb = 30, 50
+        cols = 24 * nb
+        coords, _ = _all_class_coords(rows, nb, 5)
+        scale, tail = synth.fp16_bits(np.ones(rows)), None
+    else:
+        rows, cols = 3, 11
+        coords = np.zeros((3, 0, 24), np.int8)
+        scale, tail = synth.fp16_bits(np.ones(rows)), synth.fp16_bits(np.ones((rows, 11)))
+    blob = lvq.expand_onehot(coords, scale, tail, rows, cols)
+    assert blob.size == lvq.layout_bytes_onehot(rows, cols) == layout.sections_onehot(rows, cols)["total"]
+    u = layout.unpack_onehot(blob, rows, cols)
+    assert np.array_equal(u["coords"], coords)
+    assert np.array_equal(u["table"], lvq.class_table())
+    assert np.array_equal(u["scale"], scale)
+    if tail is not None:
+        assert np.array_equal(u["tail"], tail)
+    assert np.all(u["words"].astype(np.int64) & 0x80008000 == 0)
+
+
+def test_gemv_onehot_validates_before_launch():
+    lib = lvq.library()
+    A = 1 << 20
+    g = lib.lvq_gemv_onehot
+    assert g(None, 4, 48, A, A, 1, None) == lvq.LVQ_E_NULL
+    assert g(A + 4, 4, 48, A, A, 1, None) == lvq.LVQ_E_ALIGN
+    assert g(A, 4, 48, A, A, 0, None) == lvq.LVQ_E_BATCH
+    assert g(A, -1, 48, A, A, 1, None) == lvq.LVQ_E_SHAPE
+    assert g(A, 0, 48, A, A, 1, None) == lvq.LVQ_OK
+    x = np.zeros((1, 1, 24), dtype=np.int8)
+    x[0, 0, :2] = (2, 2)  # not a lattice point
+    with pytest.raises(lvq.LvqError) as e:
+        lvq.expand_onehot(x, synth.fp16_bits([1.0]), None, 1, 24)
+    assert e.value.code == lvq.LVQ_E_NOT_LEECH and e.value.index == (0, 0)

@@ -3,7 +3,8 @@
 bit against the LP3 kernel on the same matrix (both decode to the same fp16
 values and sum in the same column order); LP2X with its side channel; the
 table-free direct layout against the oracle, and its results independent of
-the batch size (so of the blocks per lane the launch picks)."""
+the batch size (so of the blocks per lane the launch picks); the one-hot
+layout against the oracle and bit for bit against the direct layout."""
 import numpy as np
 import pytest
 
@@ -152,6 +153,53 @@ def test_direct_gemv_every_class():
          "tail": synth.fp16_bits(rng.standard_normal((rows, 3)) * 0.02)}
     x = synth.activations(cols, 4, 6, key=(33,))
     y = _direct(d, rows, cols, x, 4)
+    w = og.leech_weights(d["coords"], d["scale"], d["tail"], cols)
+    y64, bound = og.gemv(w, x)
+    assert og.check(y, y64, bound) <= 1.0
+
+
+def _onehot(d, rows, cols, x, batch):
+    yd = empty((batch, rows), np.float32)
+    lvq.gemv_onehot(to_dev(lvq.expand_onehot(d["coords"], d["scale"], d["tail"], rows, cols)),
+                    rows, cols, to_dev(x), yd, batch)
+    return to_host(yd, np.float32)
+
+
+@pytest.mark.parametrize("rows,cols,cfg,batch", [
+    (4096, 12288, 4, 1), (4096, 12288, 6, 4), (12288, 4096, 3, 1), (4096, 4096, 6, 2),
+    (1536, 1536, 1, 3), (130, 24 * 65 + 7, 3, 3), (257, 24 * 129, 6, 1), (5, 23, 3, 1),
+])
+def test_onehot_gemv(rows, cols, cfg, batch):
+    """Against the oracle, and bit for bit against the direct layout: both
+    decode to the same fp16 pairs and sum them in the same order."""
+    d = synth.leech_matrix(rows, cols, cfg, key=(rows, cols, cfg, 17))
+    x = synth.activations(cols, batch, cfg, rows=rows)
+    y = _onehot(d, rows, cols, x, batch)
+    w = og.leech_weights(d["coords"], d["scale"], d["tail"], cols)
+    y64, bound = og.gemv(w, x)
+    r = og.check(y, y64, bound)
+    print("onehot %dx%d cfg%d b%d: max |err| / (1e-4 * bound) = %.3g" % (rows, cols, cfg, batch, r),
+          flush=True)
+    assert r <= 1.0
+    assert np.array_equal(y.view(np.uint32), _direct(d, rows, cols, x, batch).view(np.uint32))
+
+
+def test_onehot_gemv_every_class():
+    rng = np.random.default_rng(34)
+    rows, nb = 96, 40
+    ids = rng.integers(0, leech.NUM_CLASSES, rows * nb)
+    cl = leech.classes()
+    coords = np.zeros((rows * nb, 24), dtype=np.int8)
+    for cid in np.unique(ids):
+        sel = np.nonzero(ids == cid)[0]
+        if cid:
+            coords[sel] = synth.sample_class(cl[cid]["key"], sel.size, rng)
+    cols = 24 * nb + 5
+    d = {"coords": coords.reshape(rows, nb, 24),
+         "scale": synth.fp16_bits(np.abs(rng.standard_normal(rows)) * 0.02),
+         "tail": synth.fp16_bits(rng.standard_normal((rows, 5)) * 0.02)}
+    x = synth.activations(cols, 3, 6, key=(34,))
+    y = _onehot(d, rows, cols, x, 3)
     w = og.leech_weights(d["coords"], d["scale"], d["tail"], cols)
     y64, bound = og.gemv(w, x)
     assert og.check(y, y64, bound) <= 1.0
