@@ -259,21 +259,26 @@ __device__ __forceinline__ uint32_t weight_bytes(uint32_t n) {
   return M == kNoWeights ? 0u : n;
 }
 
-// A lane's byte offset, opaque to the optimiser for this item.  Without it
-// the offsets of the item's loads (lane * size + u * 64 * size + 4 k) are loop
-// invariants, hoisted into one register each: a register per load, and loads
-// the backend can no longer merge (three dword loads per block instead of one
-// dwordx3).  Computed afresh per item, the constants fold into the loads'
-// immediate offsets and every load of the item shares one address register.
-__device__ __forceinline__ int lane_offset(int lane, int size) {
-  int o = lane * size;
-  asm volatile("" : "+v"(o));
-  return o;
+// A lane's byte offsets into an item's class ids / tail values (2 bytes per
+// lane) and code records, opaque to the optimiser once per item.  Without
+// that the offsets of the item's loads (lane * size + u * 64 * size + 4 k) are
+// loop invariants, hoisted into one register each: a register per load, and
+// loads the backend can no longer merge (three dword loads per block instead
+// of one dwordx3).  Passed through an empty asm statement per item (in place:
+// the registers are loop-carried, so no copy), the constants fold into the
+// loads' immediate offsets and every load of the item shares one register.
+struct LaneOff {
+  int meta, codes;
+};
+__device__ __forceinline__ int opaque(int& v) {
+  asm volatile("" : "+v"(v));
+  return v;
 }
 
 template <int BPL, int M>
 __device__ __forceinline__ void load_meta(const MatSet& ms, int nb, int tau, int gr, int chunk,
-                                          int lane, ItemRegs<BPL, M>& g) {
+                                          LaneOff& lo, ItemRegs<BPL, M>& g) {
+  const int lo2 = opaque(lo.meta);
   const int m = mat_of<M>(ms, gr);
   const int r = gr - start_of<M>(ms, m);
   const uint16_t* cls = pick<M>(ms, m, [](const MatSet& s, int i) { return s.v[i].cls; });
@@ -283,13 +288,12 @@ __device__ __forceinline__ void load_meta(const MatSet& ms, int nb, int tau, int
   if (M != kLp2 && M != kDirect) {  // LP2 keeps the class in the record; direct has none
     const auto rc =
         buffer_rsrc(cls + (size_t)r * nb + k0, weight_bytes<M>((uint32_t)(nb - k0) * 2));
-    const int lo = lane_offset(lane, 2);
 #pragma unroll
     for (int u = 0; u < BPL; ++u)
-      g.c[u] = __builtin_amdgcn_raw_buffer_load_b16(rc, lo + u * (kWave * 2), 0, kStream);
+      g.c[u] = __builtin_amdgcn_raw_buffer_load_b16(rc, lo2 + u * (kWave * 2), 0, kStream);
   }
   const auto rt = buffer_rsrc(tail + (size_t)r * tau, weight_bytes<M>((uint32_t)tau * 2));
-  g.tail = __builtin_amdgcn_raw_buffer_load_b16(rt, lane * 2, 0, 0);
+  g.tail = __builtin_amdgcn_raw_buffer_load_b16(rt, lo2, 0, 0);
   // the row scale, read by every lane (one transaction); a vector load, so
   // that waiting for it never holds up the LDS reads
   const auto rs = buffer_rsrc(scale + r, weight_bytes<M>(2));
@@ -297,10 +301,13 @@ __device__ __forceinline__ void load_meta(const MatSet& ms, int nb, int tau, int
 }
 
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef const __attribute__((address_space(3))) uint32_t lds_u32;
+typedef const __attribute__((address_space(3))) u32x4_t lds_u32x4;
 
 template <int BPL, int M>
-__device__ __forceinline__ void load_codes(const MatSet& ms, int nb, int gr, int chunk, int lane,
-                                           ItemRegs<BPL, M>& g) {
+__device__ __forceinline__ void load_codes(const MatSet& ms, int nb, int gr, int chunk,
+                                           LaneOff& loff, ItemRegs<BPL, M>& g) {
+  const int lo = opaque(loff.codes);
   const int m = mat_of<M>(ms, gr);
   const int r = gr - start_of<M>(ms, m);
   const uint32_t* codes = pick<M>(ms, m, [](const MatSet& s, int i) { return s.v[i].codes; });
@@ -308,7 +315,6 @@ __device__ __forceinline__ void load_codes(const MatSet& ms, int nb, int gr, int
   if constexpr (M == kDirect || M == kOneHot) {
     // one 16-byte record per block
     const auto rw = buffer_rsrc(codes + ((size_t)r * nb + k0) * 4, (uint32_t)(nb - k0) * 16);
-    const int lo = lane_offset(lane, 16);
 #pragma unroll
     for (int u = 0; u < BPL; ++u) {
       const auto v = __builtin_bit_cast(
@@ -322,7 +328,6 @@ __device__ __forceinline__ void load_codes(const MatSet& ms, int nb, int gr, int
   } else {
   const auto rw = buffer_rsrc(codes + ((size_t)r * nb + k0) * 3,
                               weight_bytes<M>((uint32_t)(nb - k0) * 12));
-  const int lo = lane_offset(lane, 12);
 #pragma unroll
   for (int u = 0; u < BPL; ++u) {
     const int o = lo + u * (kWave * 12);
@@ -336,9 +341,9 @@ __device__ __forceinline__ void load_codes(const MatSet& ms, int nb, int gr, int
 // Both groups, metadata first, so a table lookup never waits for code words.
 template <int BPL, int M>
 __device__ __forceinline__ void load_item(const MatSet& ms, int nb, int tau, int gr, int chunk,
-                                          int lane, ItemRegs<BPL, M>& g) {
-  load_meta<BPL, M>(ms, nb, tau, gr, chunk, lane, g);
-  load_codes<BPL, M>(ms, nb, gr, chunk, lane, g);
+                                          LaneOff& lo, ItemRegs<BPL, M>& g) {
+  load_meta<BPL, M>(ms, nb, tau, gr, chunk, lo, g);
+  load_codes<BPL, M>(ms, nb, gr, chunk, lo, g);
 }
 
 // LDS layout (dynamic): lut uint2[302] | x fp16 [B][kpad], kpad >= 24 * npad and
@@ -349,7 +354,8 @@ template <int B, int BPL, int M>
 __device__ __forceinline__ void decode_item(const MatSet& ms, int nb, int tau, int nchunks,
                                             int kpad, int gr, int chunk, int lane,
                                             const ItemRegs<BPL, M>& g, const uint2* lut,
-                                            const uint32_t* xs, float (&acc)[B][3]) {
+                                            const uint32_t* xs, lds_u32* xlane,
+                                            float (&acc)[B][3]) {
   asm volatile("" ::: "memory");  // keep this item's LDS reads inside this item
   // Word wi of every block goes to accumulator wi: consecutive words always
   // use different registers, and each lane adds its blocks in column order
@@ -357,7 +363,9 @@ __device__ __forceinline__ void decode_item(const MatSet& ms, int nb, int tau, i
   // row's result does not depend on the launch geometry (or on which other
   // matrices share the launch).
   const int npair = kpad / 2;
-  const uint32_t* xl = xs + (chunk * (kWave * BPL) + lane) * 12;
+  // x through a 32-bit LDS pointer (this lane's base, set once per kernel):
+  // one add per item for its address
+  lds_u32* xl = xlane + chunk * (kWave * BPL * 12);
 #pragma unroll
   for (int u = 0; u < BPL; ++u) {
     if constexpr (M == kDirect) {
@@ -367,8 +375,8 @@ __device__ __forceinline__ void decode_item(const MatSet& ms, int nb, int tau, i
       const uint32_t pp = (g.w[u][0] & 1u) * 0x00010001u;
 #pragma unroll
       for (int bb = 0; bb < B; ++bb) {
-        const uint4* xb = (const uint4*)(xl + bb * npair + u * (kWave * 12));
-        const uint4 q0 = xb[0], q1 = xb[1], q2 = xb[2];
+        lds_u32x4* xb = (lds_u32x4*)(xl + bb * npair + u * (kWave * 12));
+        const u32x4_t q0 = xb[0], q1 = xb[1], q2 = xb[2];
         const uint32_t xp[12] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w,
                                  q2.x, q2.y, q2.z, q2.w};
 #pragma unroll
@@ -394,8 +402,8 @@ __device__ __forceinline__ void decode_item(const MatSet& ms, int nb, int tau, i
       for (int i = 0; i < 4; ++i) dm[i] = (l.y >> (8 * i)) & 0xFFu;
 #pragma unroll
       for (int bb = 0; bb < B; ++bb) {
-        const uint4* xb = (const uint4*)(xl + bb * npair + u * (kWave * 12));
-        const uint4 q0 = xb[0], q1 = xb[1], q2 = xb[2];
+        lds_u32x4* xb = (lds_u32x4*)(xl + bb * npair + u * (kWave * 12));
+        const u32x4_t q0 = xb[0], q1 = xb[1], q2 = xb[2];
         const uint32_t xp[12] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w,
                                  q2.x, q2.y, q2.z, q2.w};
 #pragma unroll
@@ -426,7 +434,7 @@ __device__ __forceinline__ void decode_item(const MatSet& ms, int nb, int tau, i
                           : leech_pair(g.w[u][wi], vi, l.x, l.y);
 #pragma unroll
       for (int bb = 0; bb < B; ++bb) {
-        const uint4 xq = *(const uint4*)(xl + bb * npair + u * (kWave * 12) + 4 * wi);
+        const u32x4_t xq = *(lds_u32x4*)(xl + bb * npair + u * (kWave * 12) + 4 * wi);
         if (M == kGain) {
           // the word's partial sum, times its block's gain
           float pw = dot2(d[0], xq.x, 0.f);
@@ -687,11 +695,13 @@ leech_gemv_kernel(MatSet ms, int rows, int nb, int tau, int cols, int nchunks, i
   //    uses, so that the load sequence has no branches and every later wait
   //    counts exactly)
   ItemRegs<BPL, M> ia, ib;
+  LaneOff lo = {lane * 2, lane * 4 * words_of(M)};
+  lds_u32* const xlane = (lds_u32*)xs + lane * 12;
   int ra = wave < rows ? wave : 0, ca = 0;
   int rb = ca + 1 == nchunks ? ra + nwaves : ra, cb = ca + 1 == nchunks ? 0 : ca + 1;
   if (items < 2) { rb = ra; cb = ca; }
-  load_item<BPL, M>(ms, nb, tau, ra, ca, lane, ia);
-  load_item<BPL, M>(ms, nb, tau, rb, cb, lane, ib);
+  load_item<BPL, M>(ms, nb, tau, ra, ca, lo, ia);
+  load_item<BPL, M>(ms, nb, tau, rb, cb, lo, ib);
   asm volatile("" ::: "memory");
   // 3. the class table into LDS; the barrier also waits for x
   for (int c = tid; M != kDirect && c < LVQ_NUM_CLASSES; c += nthr) {
@@ -721,23 +731,23 @@ leech_gemv_kernel(MatSet ms, int rows, int nb, int tau, int cols, int nchunks, i
   };
   int j = 0;
   for (; j + 3 < items; j += 2) {
-    decode_item<B, BPL, M>(ms, nb, tau, nchunks, kpad, ra, ca, lane, ia, lut, xs, acc);
+    decode_item<B, BPL, M>(ms, nb, tau, nchunks, kpad, ra, ca, lane, ia, lut, xs, xlane, acc);
     advance(ra, ca);
-    load_item<BPL, M>(ms, nb, tau, ra, ca, lane, ia);
-    decode_item<B, BPL, M>(ms, nb, tau, nchunks, kpad, rb, cb, lane, ib, lut, xs, acc);
+    load_item<BPL, M>(ms, nb, tau, ra, ca, lo, ia);
+    decode_item<B, BPL, M>(ms, nb, tau, nchunks, kpad, rb, cb, lane, ib, lut, xs, xlane, acc);
     advance(rb, cb);
-    load_item<BPL, M>(ms, nb, tau, rb, cb, lane, ib);
+    load_item<BPL, M>(ms, nb, tau, rb, cb, lo, ib);
   }
   // the last one to three items
-  decode_item<B, BPL, M>(ms, nb, tau, nchunks, kpad, ra, ca, lane, ia, lut, xs, acc);
+  decode_item<B, BPL, M>(ms, nb, tau, nchunks, kpad, ra, ca, lane, ia, lut, xs, xlane, acc);
   if (j + 2 < items) {
     advance(ra, ca);
-    load_item<BPL, M>(ms, nb, tau, ra, ca, lane, ia);
+    load_item<BPL, M>(ms, nb, tau, ra, ca, lo, ia);
   }
   if (j + 1 < items)
-    decode_item<B, BPL, M>(ms, nb, tau, nchunks, kpad, rb, cb, lane, ib, lut, xs, acc);
+    decode_item<B, BPL, M>(ms, nb, tau, nchunks, kpad, rb, cb, lane, ib, lut, xs, xlane, acc);
   if (j + 2 < items)
-    decode_item<B, BPL, M>(ms, nb, tau, nchunks, kpad, ra, ca, lane, ia, lut, xs, acc);
+    decode_item<B, BPL, M>(ms, nb, tau, nchunks, kpad, ra, ca, lane, ia, lut, xs, xlane, acc);
 }
 
 // LP2X side channel: after the LP2 kernel (whose records for these blocks are
