@@ -363,9 +363,14 @@ __device__ __forceinline__ void decode_item(const MatSet& ms, int nb, int tau, i
   // row's result does not depend on the launch geometry (or on which other
   // matrices share the launch).
   const int npair = kpad / 2;
-  // x through a 32-bit LDS pointer (this lane's base, set once per kernel):
-  // one add per item for its address
-  lds_u32* xl = xlane + chunk * (kWave * BPL * 12);
+  // The 16 bytes of x at 32-bit word o of the lane's x (word 0 = the pair
+  // feeding view 0 of code word 0 of this item's first block, batch row 0),
+  // through a 32-bit LDS pointer.  Batch 1 starts from this lane's base, set
+  // once per kernel (one add per item); above batch 1 that extra live register
+  // pushes the 64-VGPR variants into spills, so the address is formed per item.
+  lds_u32* xl = B == 1 ? xlane + chunk * (kWave * BPL * 12)
+                       : (lds_u32*)xs + (chunk * (kWave * BPL) + lane) * 12;
+  auto xq = [&](int o) -> u32x4_t { return *(lds_u32x4*)(xl + o); };
 #pragma unroll
   for (int u = 0; u < BPL; ++u) {
     if constexpr (M == kDirect) {
@@ -375,8 +380,8 @@ __device__ __forceinline__ void decode_item(const MatSet& ms, int nb, int tau, i
       const uint32_t pp = (g.w[u][0] & 1u) * 0x00010001u;
 #pragma unroll
       for (int bb = 0; bb < B; ++bb) {
-        lds_u32x4* xb = (lds_u32x4*)(xl + bb * npair + u * (kWave * 12));
-        const u32x4_t q0 = xb[0], q1 = xb[1], q2 = xb[2];
+        const int o = bb * npair + u * (kWave * 12);
+        const u32x4_t q0 = xq(o), q1 = xq(o + 4), q2 = xq(o + 8);
         const uint32_t xp[12] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w,
                                  q2.x, q2.y, q2.z, q2.w};
 #pragma unroll
@@ -402,8 +407,8 @@ __device__ __forceinline__ void decode_item(const MatSet& ms, int nb, int tau, i
       for (int i = 0; i < 4; ++i) dm[i] = (l.y >> (8 * i)) & 0xFFu;
 #pragma unroll
       for (int bb = 0; bb < B; ++bb) {
-        lds_u32x4* xb = (lds_u32x4*)(xl + bb * npair + u * (kWave * 12));
-        const u32x4_t q0 = xb[0], q1 = xb[1], q2 = xb[2];
+        const int o = bb * npair + u * (kWave * 12);
+        const u32x4_t q0 = xq(o), q1 = xq(o + 4), q2 = xq(o + 8);
         const uint32_t xp[12] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w,
                                  q2.x, q2.y, q2.z, q2.w};
 #pragma unroll
@@ -434,20 +439,20 @@ __device__ __forceinline__ void decode_item(const MatSet& ms, int nb, int tau, i
                           : leech_pair(g.w[u][wi], vi, l.x, l.y);
 #pragma unroll
       for (int bb = 0; bb < B; ++bb) {
-        const u32x4_t xq = *(lds_u32x4*)(xl + bb * npair + u * (kWave * 12) + 4 * wi);
+        const u32x4_t xv = xq(bb * npair + u * (kWave * 12) + 4 * wi);
         if (M == kGain) {
           // the word's partial sum, times its block's gain
-          float pw = dot2(d[0], xq.x, 0.f);
-          pw = dot2(d[1], xq.y, pw);
-          pw = dot2(d[2], xq.z, pw);
-          pw = dot2(d[3], xq.w, pw);
+          float pw = dot2(d[0], xv.x, 0.f);
+          pw = dot2(d[1], xv.y, pw);
+          pw = dot2(d[2], xv.z, pw);
+          pw = dot2(d[3], xv.w, pw);
           acc[bb][wi] = __builtin_fmaf(pw, gam, acc[bb][wi]);
         } else {
           float& a = acc[bb][wi];
-          a = dot2(d[0], xq.x, a);
-          a = dot2(d[1], xq.y, a);
-          a = dot2(d[2], xq.z, a);
-          a = dot2(d[3], xq.w, a);
+          a = dot2(d[0], xv.x, a);
+          a = dot2(d[1], xv.y, a);
+          a = dot2(d[2], xv.z, a);
+          a = dot2(d[3], xv.w, a);
         }
       }
     }
@@ -554,18 +559,167 @@ __device__ __forceinline__ void rot_lds_pass(uint16_t* xh, float* fb, const uint
   }
 }
 
+// Stages s .. s + R - 1 (s >= 4) of the MM sequences of K values in fb,
+// coordinates 2^s apart: consecutive threads take consecutive sets, so
+// consecutive addresses.  The last pass scales, rounds and writes fp16 x at
+// c MM + b.
+template <int R, int MM>
+__device__ __forceinline__ void rot_fb_pass(uint16_t* xh, float* fb, int logk, int s, bool last,
+                                            float scale, int tid, int nthr) {
+  constexpr int kR = 1 << R;
+  const int lsets = logk - R;  // log2 of the sets per sequence
+  const int low = (1 << s) - 1;
+  for (int sg = tid; sg < (MM << lsets); sg += nthr) {
+    const int b = MM == 1 ? 0 : sg >> lsets;
+    const int set = sg & ((1 << lsets) - 1);
+    const int c0 = ((set & ~low) << R) | (set & low);
+    float* f = fb + (b << logk) + c0;
+    float v[kR];
+#pragma unroll
+    for (int t = 0; t < kR; ++t) v[t] = f[t << s];
+    rot_set_stages<R>(v);
+    if (last) {
+#pragma unroll
+      for (int t = 0; t < kR; ++t) xh[(c0 + (t << s)) * MM + b] = rot_out(v[t], scale);
+    } else {
+#pragma unroll
+      for (int t = 0; t < kR; ++t) f[t << s] = v[t];
+    }
+  }
+}
+
+// The rotation of one batch row for K >= 16 and m = MM <= 8.  1: the signs go
+// into the staged x in place (16-byte units).  2: task L = b K/16 + c16 takes
+// values 16 c16 .. 16 c16 + 15 of sequence b: for m = 1 two 16-byte reads of
+// x, for m > 1 the Q mix of the 16 groups (32 m contiguous bytes of x, eight
+// groups at a time) in registers, in lvq_rotate's fma order; stages 0-3 in
+// registers; the 16 values to the f32 buffer (for m = 1 and K = 16, the
+// result straight back to x).  3: radix passes for stages 4 and up, threads
+// on consecutive sets (consecutive addresses); the last pass scales, rounds
+// and writes x at c m + b (m > 1, K = 16: a copy pass does that).  Every
+// stage is the same butterflies on the same operands as everywhere else, so
+// the result is lvq_rotate's bit for bit.
+template <int MM>
+__device__ __forceinline__ void rotate_x_regs(uint16_t* xh, float* fb, const float* qs, const uint32_t* signs,
+                              const MatSet& ms, int cols, int tid, int nthr) {
+  const int logk = ms.rot_logk;
+  float scale = ms.rot_scale;
+  if (MM == 1 && qs) scale *= qs[0];
+  if (signs) {
+    for (int j8 = tid; j8 < (cols >> 3); j8 += nthr) {
+      uint4* p = (uint4*)(xh + 8 * j8);
+      *p = rot_apply_signs(*p, signs[j8 >> 2] >> ((j8 & 3) * 8));
+    }
+    __syncthreads();
+  }
+  // the 16-byte unit of x holding coordinates 8 j8 .. 8 j8 + 7
+  auto unit = [&](int j8) { return *(const uint4*)(xh + 8 * j8); };
+  const int lck = logk - 4;  // log2 of the 16-value chunks per sequence
+  const bool direct = MM == 1 && logk == 4;
+  for (int l = tid; l < (MM << lck); l += nthr) {
+    const int b = MM == 1 ? 0 : l >> lck;
+    const int c16 = l & ((1 << lck) - 1);
+    float v[16];
+    if (MM == 1) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const uint4 u = unit(2 * c16 + h);
+        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          v[8 * h + 2 * i] = rot_half((uint16_t)w[i]);
+          v[8 * h + 2 * i + 1] = rot_half((uint16_t)(w[i] >> 16));
+        }
+      }
+    } else {
+      float qrow[MM];
+#pragma unroll
+      for (int d = 0; d < MM; ++d) qrow[d] = qs ? qs[b * MM + d] : (d == b ? 1.f : 0.f);
+      // groups g0 .. g0 + 7 (16 MM contiguous bytes) mixed into o[8]
+      auto mix8 = [&](int g0, float* o) {
+        uint32_t w[4 * MM];
+#pragma unroll
+        for (int i = 0; i < MM; ++i) {
+          const uint4 u = unit(g0 * MM / 8 + i);
+          w[4 * i] = u.x;
+          w[4 * i + 1] = u.y;
+          w[4 * i + 2] = u.z;
+          w[4 * i + 3] = u.w;
+        }
+#pragma unroll
+        for (int g = 0; g < 8; ++g) {
+          float a = 0.f;
+#pragma unroll
+          for (int d = 0; d < MM; ++d) {
+            const int e = g * MM + d;
+            a = __builtin_fmaf(qrow[d], rot_half((uint16_t)(w[e >> 1] >> (16 * (e & 1)))), a);
+          }
+          o[g] = a;
+        }
+      };
+      mix8(16 * c16, v);
+      asm volatile("" ::: "memory");  // one half's words live at a time
+      mix8(16 * c16 + 8, v + 8);
+    }
+    rot_set_stages<4>(v);
+    if (direct) {
+      uint32_t o[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        o[i] = rot_out(v[2 * i], scale) | ((uint32_t)rot_out(v[2 * i + 1], scale) << 16);
+      *(uint4*)(xh + 16 * c16) = make_uint4(o[0], o[1], o[2], o[3]);
+      *(uint4*)(xh + 16 * c16 + 8) = make_uint4(o[4], o[5], o[6], o[7]);
+    } else {
+      float4* f = (float4*)(fb + (b << logk) + 16 * c16);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) f[i] = make_float4(v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]);
+    }
+  }
+  __syncthreads();
+  if (direct) return;
+  if (logk == 4) {  // m > 1, K = 16: the values are final; scale, round, interleave
+    for (int c = tid; c < (MM << 4); c += nthr) xh[(c & 15) * MM + (c >> 4)] = rot_out(fb[c], scale);
+    __syncthreads();
+    return;
+  }
+  for (int st = 4; st < logk; st += 4) {
+    const int r = logk - st < 4 ? logk - st : 4;
+    const bool last = st + r == logk;
+    if (r == 4) rot_fb_pass<4, MM>(xh, fb, logk, st, last, scale, tid, nthr);
+    else if (r == 3) rot_fb_pass<3, MM>(xh, fb, logk, st, last, scale, tid, nthr);
+    else if (r == 2) rot_fb_pass<2, MM>(xh, fb, logk, st, last, scale, tid, nthr);
+    else rot_fb_pass<1, MM>(xh, fb, logk, st, last, scale, tid, nthr);
+    __syncthreads();
+  }
+}
+
 // One batch row of the staged x (fp16, in LDS, zero past cols) rotated in
 // place.  The butterflies are lvq_rotate's, stage by stage in the same order on
 // the same operands (only where the values live differs), and so is the Q mix,
-// so the result is that kernel's output bit for bit.  Q mix: a thread takes
-// whole groups of m coordinates, the Q row entries are uniform (scalar loads);
-// then radix-16 passes over the K-point sequences in LDS, one barrier each.
-// Every thread of the workgroup takes part; ends with a barrier.
-__device__ void rotate_x_lds(uint16_t* xh, float* fb, const float* qs, const uint32_t* signs,
+// so the result is that kernel's output bit for bit.  K >= 16 and m <= 8 (every
+// Qwen3 width but 25600) take rotate_x_regs; otherwise a thread takes whole
+// groups of m coordinates for the Q mix, then radix-16 passes over the K-point
+// sequences in LDS, one barrier each.  Every thread of the workgroup takes
+// part; ends with a barrier.
+__device__ __forceinline__ void rotate_x_lds(uint16_t* xh, float* fb, const float* qs, const uint32_t* signs,
                              const MatSet& ms, int cols, int tid, int nthr) {
   // qs and signs are the LDS copies (or null); no global load here, so
   // nothing waits on the weight loads in flight
   const int m = ms.rot_m, logk = ms.rot_logk;
+  if (logk >= 4) {  // uniform
+    switch (m) {
+      case 1: return rotate_x_regs<1>(xh, fb, qs, signs, ms, cols, tid, nthr);
+      case 2: return rotate_x_regs<2>(xh, fb, qs, signs, ms, cols, tid, nthr);
+      case 3: return rotate_x_regs<3>(xh, fb, qs, signs, ms, cols, tid, nthr);
+      case 4: return rotate_x_regs<4>(xh, fb, qs, signs, ms, cols, tid, nthr);
+      case 5: return rotate_x_regs<5>(xh, fb, qs, signs, ms, cols, tid, nthr);
+      case 6: return rotate_x_regs<6>(xh, fb, qs, signs, ms, cols, tid, nthr);
+      case 7: return rotate_x_regs<7>(xh, fb, qs, signs, ms, cols, tid, nthr);
+      case 8: return rotate_x_regs<8>(xh, fb, qs, signs, ms, cols, tid, nthr);
+      default: break;
+    }
+  }
+  // K < 16 or m > 8: passes over LDS
   const int k = cols / m;
   float scale = ms.rot_scale;
   if (m == 1 && qs) scale *= qs[0];

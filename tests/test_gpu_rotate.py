@@ -92,17 +92,25 @@ def test_rotate_in_place_and_exact_cases():
     assert np.all(np.abs(a - b) <= 2 * orot.ulp16(a) + 1e-3)
 
 
-@pytest.mark.parametrize("rows,n,m,batch", [
-    (4096, 4096, 1, 1), (4096, 12288, 3, 1), (4096, 12288, 3, 4), (1024, 25600, 25, 1),
-    (300, 2560, 5, 2), (257, 1024 * 19, 19, 1), (64, 256, 1, 3), (96, 24 * 64, 3, 2),
+@pytest.mark.parametrize("rows,n,m,batch,signs,q", [
+    (4096, 4096, 1, 1, True, True), (4096, 12288, 3, 1, True, True),
+    (4096, 12288, 3, 4, True, True), (1024, 25600, 25, 1, True, True),
+    (300, 2560, 5, 2, True, True), (257, 1024 * 19, 19, 1, True, True),
+    (64, 256, 1, 3, True, True), (96, 24 * 64, 3, 2, True, True),
+    # K from 8 to 64 (lane groups narrower than a wave), every m up to 8, no
+    # signs or no Q
+    (50, 24, 3, 1, True, True), (64, 48, 6, 2, True, True), (128, 192, 3, 1, True, True),
+    (128, 16384, 8, 1, True, True), (200, 2048, 2, 3, True, False),
+    (77, 1792, 7, 1, False, True), (64, 4096, 1, 2, False, False), (96, 24 * 64, 3, 2, False, False),
+    (40, 4 * 32, 4, 1, True, True),
 ])
-def test_gemv_rotated_equals_rotate_then_gemv(rows, n, m, batch):
+def test_gemv_rotated_equals_rotate_then_gemv(rows, n, m, batch, signs, q):
     import synth as sy
     from oracle import gemv as og
     d = sy.leech_matrix(rows, n, 3, key=(rows, n, m))
     blob = to_dev(lvq.expand(d["coords"], d["scale"], d["tail"], rows, n))
-    x, words, qm = _case(n, m, batch, seed=rows + n)
-    wd = to_dev(words)
+    x, words, qm = _case(n, m, batch, seed=rows + n, signs=signs, q=q)
+    wd = None if words is None else to_dev(words)
     qd = None if qm is None else to_dev(qm)
     xr = empty((batch, n), np.uint16)
     lvq.rotate(to_dev(x), n, m, wd, qd, xr, batch)
