@@ -15,7 +15,9 @@ so the 256 MB Infinity Cache never serves them.
 
 Beside the headline the JSON line carries one record per arm x config x
 batch (Leech at every config shape and batch 1 and 4, the BPDQ and bitshift-
-trellis arms, the fp16 dense control at the same shapes), each with its
+trellis arms, the fp16 dense control at the same shapes, the rotation and
+the rotated GEMV, the shape-gain GEMV, the LP2, LP2X, direct and one-hot
+layouts, load-time unfolding of 48-bit words), each with its
 fraction of a read-only streaming kernel over the same bytes and rotation
 (lvq_stream_read), the metric shape captured in a HIP graph, the Qwen3-8B
 Leech stack of 252 GEMVs (GEMV-only time on precomputed inputs, and the
@@ -164,10 +166,19 @@ def to_dev(torch, a):
     return torch.from_numpy(np.ascontiguousarray(a).view(view)).to("cuda")
 
 
+def code_text(src):
+    """Source text without comments and with whitespace collapsed: what the
+    compiler sees, so that a comment edit does not stale a profile."""
+    src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", " ", src)
+    return re.sub(r"\s+", " ", src).strip()
+
+
 def kernel_sha():
     h = hashlib.sha256()
     for f in ("lvq_gemv.hip", "common.h", "layout.h"):
-        h.update(open(os.path.join(ROOT, "dequant_gemv_lvq_amd", "csrc", f), "rb").read())
+        src = open(os.path.join(ROOT, "dequant_gemv_lvq_amd", "csrc", f)).read()
+        h.update(code_text(src).encode())
     return h.hexdigest()[:16]
 
 

@@ -1,7 +1,12 @@
-// Offline expander: integer Leech-lattice blocks -> packed bit-plane blob.
+// Offline expander: integer Leech-lattice blocks -> packed blobs.
 //
-// Host-only C++ (no HIP call).  Implements lvq_class_table, lvq_layout_bytes,
-// lvq_expand, lvq_strerror and lvq_last_error_index of include/lvq.h.
+// Host-only C++ (no HIP call).  Implements lvq_class_table, lvq_strerror,
+// lvq_last_error_index and the expanders and blob sizes of include/lvq.h: the
+// served LP3 layout (lvq_expand, with the shape-gain bit: lvq_expand_gain),
+// LP2 and LP2X (two rank planes, with the exception side channel), the
+// table-free direct layout and the one-hot rank-mask layout.  Every expander
+// validates each block (membership and the shell-12 limit) and reports the
+// first offending one.
 //
 // Source: arXiv 2609.02652, section 1 (contributions C1 and C2): lattice
 // codes are unfolded at load time into divergence-free layouts whose decode

@@ -1,4 +1,10 @@
-// Fused Leech-lattice dequantize-plus-matvec for gfx950 (lvq_gemv, lvq_decode).
+// Fused Leech-lattice dequantize-plus-matvec for gfx950: lvq_gemv and its
+// variants over one kernel template (modes): the fused multi-matrix launch
+// and the no-weights control (lvq_gemv_fused, lvq_gemv_noweights), the
+// shape-gain GEMV (lvq_gemv_gain), the compact and alternative layouts
+// (lvq_gemv_lp2, lvq_gemv_lp2x with its side-channel kernel, lvq_gemv_direct,
+// lvq_gemv_onehot), the rotation in the prologue (lvq_gemv_rotated), and the
+// lvq_decode test hook.
 //
 // Source: arXiv 2609.02652, section 1, contribution C1: a fused kernel reads
 // the unfolded layout with shifts, masks and a predicated table lookup, the
@@ -9,22 +15,24 @@
 //
 // gfx950 design.  One wave64 owns one row at a time (rows are grid-strided
 // over all waves).  Lane l takes blocks l, l + 64, ... of the row, so every
-// load instruction of a wave reads one contiguous run of the row's code words
-// (12 bytes per lane) and class ids (2 bytes per lane).  The loads are raw
-// buffer loads: the per-lane offset is fixed, the item's position is in the
-// scalar buffer resource, and a load past the row's end reads 0 (which
-// decodes to +0), so no vector instruction goes to addressing or masking.
-// x is copied into LDS once per workgroup by buffer loads that write LDS
-// directly (no registers, no vector instructions); the pair feeding view v of
-// code word w of block k is the natural fp16 pair at column 24k + 8w + 2v.
-// The class table is staged in LDS as 8-byte byte-LUTs.  Per coordinate pair
-// the decode is
+// load instruction of a wave reads one contiguous run of the row's code
+// records (12 bytes per lane, 16 in the direct and one-hot layouts) and class
+// ids (2 bytes per lane).  The loads are raw buffer loads: the per-lane
+// offset is fixed, the item's position is in the scalar buffer resource, and
+// a load past the row's end reads 0 (which decodes to +0), so no vector
+// instruction goes to addressing or masking.  x is copied into LDS once per
+// workgroup by buffer loads that write LDS directly (no registers, no vector
+// instructions); the pair feeding view v of code word w of block k is the
+// natural fp16 pair at column 24k + 8w + 2v.  The class table is staged in
+// LDS as 8-byte byte-LUTs.  Per coordinate pair the decode is
 //     rotate (v_alignbit), mask (v_and), byte LUT (v_perm)
 // giving two signed magnitudes as exact fp16 subnormals (value * 2^-24), and
 // one v_dot2_f32_f16 multiplies them with the x pair into an fp32
-// accumulator; the 2^24 is folded into the row scale.  No MFMA: at batch 1
-// this is a stream over HBM.  The wave reduction is a fixed DPP tree, so the
-// result does not depend on timing.
+// accumulator; the 2^24 is folded into the row scale.  No MFMA: the batch-1
+// matvec is a stream over HBM whose decode keeps the VALU about half busy
+// (54 VALU per block-lane at the metric shape).  The wave reduction is a
+// fixed DPP tree and every sum order is fixed by the columns, so the result
+// does not depend on timing or on the launch geometry.
 
 #include "common.h"
 #include "rotate_dev.h"
