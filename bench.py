@@ -2,7 +2,7 @@
 """Benchmark of the Leech-lattice dequantize-plus-matvec hot path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--trials T]
-                    [--no-arms] [--no-stack] [--no-cpu] [--profile KERNEL]
+                    [--no-arms] [--no-stack] [--no-cpu] [--profile KERNEL [--profile-batch B]]
 
 A step is one batch-1 Leech GEMV y = W x at 4096 x 12288 (down_proj-shaped,
 shells 2..6 with P(m) ~ 2^-m), the workload the metric is quoted on, on
@@ -28,7 +28,8 @@ kernel at these shapes is the GPU test suite's job; the cpu_baseline leg,
 which runs the oracle on the timed workload anyway, also reports the largest
 error ratio of the timed Leech output.
 
---profile KERNEL runs only that kernel's launch loop (for rocprofv3 counters);
+--profile KERNEL runs only that kernel's launch loop (for rocprofv3 counters;
+the Leech kinds at 4096 x 12288, batch --profile-batch);
 --profile copy runs a plain fp32->fp16 conversion of known size, the
 reference that scales the FETCH_SIZE / WRITE_SIZE counters to bytes.
 """
@@ -60,7 +61,8 @@ def parse():
     p.add_argument("--no-stack", action="store_true")
     p.add_argument("--no-cpu", action="store_true")
     p.add_argument("--stack-layers", type=int, default=QWEN_LAYERS)
-    p.add_argument("--profile", choices=["leech", "noweights", "fp16", "bpdq", "trellis", "copy"], default=None)
+    p.add_argument("--profile", choices=["leech", "noweights", "direct", "fp16", "bpdq", "trellis", "copy"], default=None)
+    p.add_argument("--profile-batch", type=int, default=1, choices=[1, 2, 3, 4])
     return p.parse_args()
 
 
@@ -745,15 +747,17 @@ def profile_only(torch, lvq, args):
         log("copy: %d fp32 -> fp16 elements per launch (reads %d B, writes %d B)"
             % (n, 4 * n, 2 * n))
         return
-    if args.profile in ("leech", "noweights"):
+    if args.profile in ("leech", "noweights", "direct"):
+        bt = args.profile_batch
         d = synth.leech_matrix(ROWS, COLS, 4)
-        blob = lvq.expand(d["coords"], d["scale"], d["tail"], ROWS, COLS)
+        ex = lvq.expand_direct if args.profile == "direct" else lvq.expand
+        blob = ex(d["coords"], d["scale"], d["tail"], ROWS, COLS)
         n = copies_for(blob.size)
         bufs = dev_copies(torch, blob, n)
-        xd = to_dev(torch, synth.activations(COLS, 1, 4, rows=ROWS))
-        yd = torch.empty((1, ROWS), dtype=torch.float32, device="cuda")
-        call = lvq.gemv if args.profile == "leech" else lvq.gemv_noweights
-        fn = lambda i: call(bufs[i % n], ROWS, COLS, xd, yd, 1)  # noqa: E731
+        xd = to_dev(torch, synth.activations(COLS, bt, 4, rows=ROWS))
+        yd = torch.empty((bt, ROWS), dtype=torch.float32, device="cuda")
+        call = {"leech": lvq.gemv, "noweights": lvq.gemv_noweights, "direct": lvq.gemv_direct}[args.profile]
+        fn = lambda i: call(bufs[i % n], ROWS, COLS, xd, yd, bt)  # noqa: E731
     elif args.profile == "fp16":
         wb = synth.dense_matrix(ROWS, COLS, cfg=2)
         n = copies_for(wb.size * 2)

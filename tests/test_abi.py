@@ -164,6 +164,8 @@ def test_device_entry_points_validate_before_launch():
     assert lib.lvq_gemv(A + 4, 4, 48, A, A, 1, None) == lvq.LVQ_E_ALIGN
     assert lib.lvq_gemv(A, -1, 48, A, A, 1, None) == lvq.LVQ_E_SHAPE
     assert lib.lvq_gemv(A, 4, 70000, A, A, 1, None) == lvq.LVQ_E_SHAPE
+    assert lib.lvq_gemv(A, 4, 65537, A, A, 1, None) == lvq.LVQ_E_SHAPE  # batch x cols > 65,536
+    assert lib.lvq_gemv(A, 4, 16385, A, A, 4, None) == lvq.LVQ_E_SHAPE
     assert lib.lvq_gemv(A, 0, 48, A, A, 1, None) == lvq.LVQ_OK  # nothing to do
     assert lib.lvq_decode(A, 4, 48, None, None) == lvq.LVQ_E_NULL
     assert lib.lvq_decode(A, 4, 48, A + 8, None) == lvq.LVQ_E_ALIGN
