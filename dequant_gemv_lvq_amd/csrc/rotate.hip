@@ -42,8 +42,9 @@ constexpr int kRotMaxM = 32;
 
 
 
-// Stages s .. s + R - 1 (s >= 9) over buf: coordinates 2^s apart, consecutive
-// threads at consecutive addresses.  The last pass scales, rounds and stores.
+// Stages s .. s + R - 1 over buf: coordinates 2^s apart, consecutive threads
+// at consecutive addresses (for s >= 4).  The last pass scales, rounds and
+// stores.
 template <int R>
 __device__ __forceinline__ void rot_high_pass(float* buf, int k, int s, bool last, int mm, int b,
                                               float scale, uint16_t* yr, int tid, int nthr) {
@@ -225,6 +226,130 @@ rotate_kernel(const uint16_t* x, const uint32_t* __restrict__ signs,
   }
 }
 
+// Workgroup (b, batch row) for K >= 16 and m = MM <= 8: y[c m + b] for c < K.
+// A thread takes 16 consecutive values of sequence b: for m = 1 two 16-byte
+// loads of x, for m > 1 the Q mix of the 16 groups (32 m contiguous bytes of
+// x, read as 16-byte loads, eight groups at a time) in registers, in the same
+// fma order as the general kernel; the signs are XORed into each 16-byte
+// unit as it arrives.  Stages 0-3 in registers, the 16 values to LDS, then
+// radix passes for stages 4 and up with consecutive threads on consecutive
+// addresses; the last pass scales, rounds and stores.  Each stage applies
+// the same butterflies to the same operands as the general kernel, so both
+// give the same bits.  No staging of x and no lane exchanges: one barrier per
+// pass.  LDS: 4 K bytes.
+template <int MM>
+__global__ void __launch_bounds__(kRotThreads)
+rotate16_kernel(const uint16_t* x, const uint32_t* __restrict__ signs,
+                const float* __restrict__ q, int n, int logk, float scale, uint16_t* y) {
+  // y may be x when m = 1: every read of the row happens before the first
+  // barrier and every write after the last one (for m > 1 the host refuses
+  // overlap)
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  float* buf = (float*)smem;
+  const int tid = threadIdx.x, nthr = blockDim.x;
+  const int b = MM == 1 ? 0 : blockIdx.x;
+  const uint16_t* xr = x + (size_t)blockIdx.y * n;
+  uint16_t* yr = y + (size_t)blockIdx.y * n;
+  if (MM == 1 && q) scale *= q[0];
+  float qrow[MM];
+#pragma unroll
+  for (int d = 0; d < MM; ++d) qrow[d] = MM == 1 ? 1.f : (q ? q[b * MM + d] : (d == b ? 1.f : 0.f));
+  // coordinates 8 j8 .. 8 j8 + 7 of the row, signs applied
+  auto unit = [&](int j8) {
+    const uint4 u = *(const uint4*)(xr + (size_t)8 * j8);
+    return signs ? rot_apply_signs(u, signs[j8 >> 2] >> ((j8 & 3) * 8)) : u;
+  };
+  const int nck = 1 << (logk - 4);
+  for (int c16 = tid; c16 < nck; c16 += nthr) {
+    float v[16];
+    if (MM == 1) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const uint4 u = unit(2 * c16 + h);
+        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          v[8 * h + 2 * i] = rot_half((uint16_t)w[i]);
+          v[8 * h + 2 * i + 1] = rot_half((uint16_t)(w[i] >> 16));
+        }
+      }
+    } else {
+      auto mix8 = [&](int g0, float* o) {  // groups g0 .. g0 + 7
+        uint32_t w[4 * MM];
+#pragma unroll
+        for (int i = 0; i < MM; ++i) {
+          const uint4 u = unit(g0 * MM / 8 + i);
+          w[4 * i] = u.x;
+          w[4 * i + 1] = u.y;
+          w[4 * i + 2] = u.z;
+          w[4 * i + 3] = u.w;
+        }
+#pragma unroll
+        for (int g = 0; g < 8; ++g) {
+          float a = 0.f;
+#pragma unroll
+          for (int d = 0; d < MM; ++d) {
+            const int e = g * MM + d;
+            a = __builtin_fmaf(qrow[d], rot_half((uint16_t)(w[e >> 1] >> (16 * (e & 1)))), a);
+          }
+          o[g] = a;
+        }
+      };
+      mix8(16 * c16, v);
+      mix8(16 * c16 + 8, v + 8);
+    }
+#pragma unroll
+    for (int h = 1; h < 16; h <<= 1) {
+#pragma unroll
+      for (int t = 0; t < 16; ++t) {
+        if (t & h) continue;
+        const float lo = v[t], hi = v[t + h];
+        v[t] = lo + hi;
+        v[t + h] = lo - hi;
+      }
+    }
+    if (logk == 4) {
+#pragma unroll
+      for (int t = 0; t < 16; ++t) yr[(size_t)(16 * c16 + t) * MM + b] = rot_out(v[t], scale);
+    } else {
+      float4* f = (float4*)(buf + 16 * c16);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) f[i] = make_float4(v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]);
+    }
+  }
+  if (logk == 4) return;  // uniform
+  __syncthreads();
+  const int k = 1 << logk;
+  for (int st = 4; st < logk; st += 4) {
+    const int r = logk - st < 4 ? logk - st : 4;
+    const bool last = st + r == logk;
+    if (r == 4) rot_high_pass<4>(buf, k, st, last, MM, b, scale, yr, tid, nthr);
+    else if (r == 3) rot_high_pass<3>(buf, k, st, last, MM, b, scale, yr, tid, nthr);
+    else if (r == 2) rot_high_pass<2>(buf, k, st, last, MM, b, scale, yr, tid, nthr);
+    else rot_high_pass<1>(buf, k, st, last, MM, b, scale, yr, tid, nthr);
+    if (!last) __syncthreads();
+  }
+}
+
+template <int MM>
+int launch_rotate16(const uint16_t* x, const uint32_t* signs, const float* q, int n, uint16_t* y,
+                    int batch, hipStream_t st) {
+  const int k = n / MM;
+  int logk = 0;
+  while ((1 << logk) < k) ++logk;
+  if (logk > 15) return LVQ_E_SHAPE;
+  const size_t lds = (size_t)k * 4;
+  if (lds > device_lds_bytes()) return LVQ_E_SHAPE;
+  // one thread per 16 values (and per radix set of the passes), whole waves
+  int threads = ((k >> 4) + kWave - 1) / kWave * kWave;
+  if (threads > kRotThreads) threads = kRotThreads;
+  const float scale = (float)(1.0 / __builtin_sqrt((double)k));
+  clear_hip_error();
+  hipLaunchKernelGGL(rotate16_kernel<MM>, dim3(MM, batch), dim3(threads), lds, st, x, signs, q, n,
+                     logk, scale, y);
+  return launch_status();
+}
+
 template <int MMAX>
 int launch_rotate(const uint16_t* x, const uint32_t* signs, const float* q, int n, int m,
                   uint16_t* y, int batch, hipStream_t st) {
@@ -273,6 +398,18 @@ extern "C" int lvq_rotate(const uint16_t* x, const uint32_t* sign_words, const f
     return LVQ_E_SHAPE;
   if (n == 0) return LVQ_OK;
   hipStream_t st = (hipStream_t)stream;
+  if (k >= 16 && m <= 8) {
+    switch (m) {
+      case 1: return launch_rotate16<1>(x, sign_words, q, n, y, batch, st);
+      case 2: return launch_rotate16<2>(x, sign_words, q, n, y, batch, st);
+      case 3: return launch_rotate16<3>(x, sign_words, q, n, y, batch, st);
+      case 4: return launch_rotate16<4>(x, sign_words, q, n, y, batch, st);
+      case 5: return launch_rotate16<5>(x, sign_words, q, n, y, batch, st);
+      case 6: return launch_rotate16<6>(x, sign_words, q, n, y, batch, st);
+      case 7: return launch_rotate16<7>(x, sign_words, q, n, y, batch, st);
+      default: return launch_rotate16<8>(x, sign_words, q, n, y, batch, st);
+    }
+  }
   if (m == 1) return launch_rotate<1>(x, sign_words, q, n, 1, y, batch, st);
   if (m <= 8) return launch_rotate<8>(x, sign_words, q, n, m, y, batch, st);
   return launch_rotate<kRotMaxM>(x, sign_words, q, n, m, y, batch, st);
