@@ -165,8 +165,9 @@ constexpr int kStream = 2;
 // to kMaxFused sharing x and the column count (lvq_gemv_fused), their rows
 // concatenated: global row g belongs to matrix m when start[m] <= g <
 // start[m + 1].  Kernel modes: single matrix, fused set, and the no-weights
-// control (the single-matrix launch with every weight load replaced by a
-// register constant: it reads x and writes y, and no weight byte).
+// control (the single-matrix launch with every weight load aimed at an empty
+// buffer range: the same instructions, it reads x and writes y, and no
+// weight byte).
 constexpr int kMaxFused = 4;
 // kGain: one matrix whose class ids carry a shape-gain bit in bit 15; the
 // block's weights are multiplied by gain[bit]
@@ -356,8 +357,10 @@ __device__ __forceinline__ void load_item(const MatSet& ms, int nb, int tau, int
 
 // LDS layout (dynamic): lut uint2[302] | x fp16 [B][kpad], kpad >= 24 * npad and
 // >= cols, a multiple of 512, with npad = nchunks * 64 * BPL blocks; columns past
-// cols are zero.  The 32-bit pair feeding view v of code word w of block k is
-// element 12k + 4w + v of a batch row (natural column order).
+// cols are zero (the rotating mode adds its f32 buffer, Q and sign words after
+// x).  The 32-bit pair feeding view v of code word w of block k is element
+// 12k + 4w + v of a batch row (natural column order; in the direct and
+// one-hot layouts pair P = 3w + v, element 12k + P).
 template <int B, int BPL, int M>
 __device__ __forceinline__ void decode_item(const MatSet& ms, int nb, int tau, int nchunks,
                                             int kpad, int gr, int chunk, int lane,
