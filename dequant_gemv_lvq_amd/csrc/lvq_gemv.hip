@@ -2,9 +2,9 @@
 // variants over one kernel template (modes): the fused multi-matrix launch
 // and the no-weights control (lvq_gemv_fused, lvq_gemv_noweights), the
 // shape-gain GEMV (lvq_gemv_gain), the compact and alternative layouts
-// (lvq_gemv_lp2, lvq_gemv_lp2x with its side-channel kernel, lvq_gemv_direct,
-// lvq_gemv_onehot), the rotation in the prologue (lvq_gemv_rotated), and the
-// lvq_decode test hook.
+// (lvq_gemv_lp2, lvq_gemv_lp2x with its side channel in each row's
+// epilogue, lvq_gemv_direct, lvq_gemv_onehot), the rotation in the prologue
+// (lvq_gemv_rotated), and the lvq_decode test hook.
 //
 // Source: arXiv 2609.02652, section 1, contribution C1: a fused kernel reads
 // the unfolded layout with shifts, masks and a predicated table lookup, the
@@ -175,8 +175,11 @@ constexpr int kMaxFused = 4;
 // kRot: one matrix whose input is first rotated, (H kron Q)(S x), in LDS
 // kDirect: one matrix in the table-free direct layout (|x| = 2h + parity)
 // kOneHot: one matrix in the one-hot layout (rank-indicator masks)
+// kLp2x: kLp2 plus the LP2X exception side channel, added in each row's
+// epilogue
 constexpr int kSingle = 0, kFused = 1, kNoWeights = 2, kGain = 3, kLp2 = 4, kRot = 5,
-              kDirect = 6, kOneHot = 7;
+              kDirect = 6, kOneHot = 7, kLp2x = 8;
+constexpr bool is_lp2(int M) { return M == kLp2 || M == kLp2x; }
 // 32-bit code words per block
 constexpr int words_of(int M) { return M == kDirect || M == kOneHot ? 4 : 3; }
 
@@ -185,6 +188,9 @@ struct MatSet {
   float* y[kMaxFused];
   int start[kMaxFused + 1];
   float gain[2];
+  // kLp2x: the side channel's row offsets and entries
+  const uint32_t* exc_off;
+  const uint4* exc;
   // kRot: the rotation of x (see lvq_rotate)
   const uint32_t* rot_signs;
   const float* rot_q;
@@ -241,6 +247,7 @@ struct ItemRegs {
   uint32_t c[BPL];
   uint32_t tail;   // this lane's tail value (0 for lanes >= tau)
   uint32_t scale;  // the row's fp16 scale
+  uint32_t e0, e1;  // kLp2x: the row's side-channel entries [e0, e1) (uniform)
 };
 
 // LP2: bytes 0..3 the first four ascending magnitudes (rank selectors 0..3),
@@ -294,7 +301,7 @@ __device__ __forceinline__ void load_meta(const MatSet& ms, int nb, int tau, int
   const uint16_t* tail = pick<M>(ms, m, [](const MatSet& s, int i) { return s.v[i].tail; });
   const uint16_t* scale = pick<M>(ms, m, [](const MatSet& s, int i) { return s.v[i].scale; });
   const int k0 = chunk * (kWave * BPL);
-  if (M != kLp2 && M != kDirect) {  // LP2 keeps the class in the record; direct has none
+  if (!is_lp2(M) && M != kDirect) {  // LP2 keeps the class in the record; direct has none
     const auto rc =
         buffer_rsrc(cls + (size_t)r * nb + k0, weight_bytes<M>((uint32_t)(nb - k0) * 2));
 #pragma unroll
@@ -307,6 +314,11 @@ __device__ __forceinline__ void load_meta(const MatSet& ms, int nb, int tau, int
   // that waiting for it never holds up the LDS reads
   const auto rs = buffer_rsrc(scale + r, weight_bytes<M>(2));
   g.scale = __builtin_amdgcn_raw_buffer_load_b16(rs, 0, 0, 0);
+  if constexpr (M == kLp2x) {
+    const auto re = buffer_rsrc(ms.exc_off + r, 8);
+    g.e0 = __builtin_amdgcn_raw_buffer_load_b32(re, 0, 0, 0);
+    g.e1 = __builtin_amdgcn_raw_buffer_load_b32(re, 4, 0, 0);
+  }
 }
 
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
@@ -437,7 +449,7 @@ __device__ __forceinline__ void decode_item(const MatSet& ms, int nb, int tau, i
     // ids < 302 by construction (lvq_expand); bit 15 is the gain bit (kGain);
     // LP2: the id sits in the odd bits 9..15 and 25..31 of word 0
     const uint32_t w0 = g.w[u][0];
-    const uint32_t cid = M == kLp2 ? (((w0 >> 9) & 0x55u) | ((w0 >> 24) & 0xAAu))
+    const uint32_t cid = is_lp2(M) ? (((w0 >> 9) & 0x55u) | ((w0 >> 24) & 0xAAu))
                        : M == kGain ? (g.c[u] & 0x7FFFu) : g.c[u];
     const uint2 l = lut[cid];
     const float gam = M == kGain ? ((g.c[u] >> 15) ? ms.gain[1] : ms.gain[0]) : 1.f;
@@ -446,7 +458,7 @@ __device__ __forceinline__ void decode_item(const MatSet& ms, int nb, int tau, i
       uint32_t d[4];
 #pragma unroll
       for (int vi = 0; vi < 4; ++vi)
-        d[vi] = M == kLp2 ? lp2_pair(g.w[u][wi], vi, l.x, l.y)
+        d[vi] = is_lp2(M) ? lp2_pair(g.w[u][wi], vi, l.x, l.y)
                           : leech_pair(g.w[u][wi], vi, l.x, l.y);
 #pragma unroll
       for (int bb = 0; bb < B; ++bb) {
@@ -469,6 +481,32 @@ __device__ __forceinline__ void decode_item(const MatSet& ms, int nb, int tau, i
     }
   }
   if (chunk == nchunks - 1) {
+    if constexpr (M == kLp2x) {
+      // the row's side-channel blocks (LP2 holds zeros there): lanes take the
+      // entries in turn, decode the LP3 code words with the class's LP3 LUT
+      // and add into their accumulators like any other block
+      const uint32_t e0 = __builtin_amdgcn_readfirstlane(g.e0);
+      const uint32_t e1 = __builtin_amdgcn_readfirstlane(g.e1);
+      if (e0 != e1) {
+        const int npair = kpad / 2;
+        for (uint32_t e = e0 + lane; e < e1; e += kWave) {
+          const uint4 ent = ms.exc[e];
+          const int k = (int)(ent.x & 0xFFFFu);
+          const uint2 l = leech_lut(ms.v[0].table[ent.x >> 16]);  // never class 0
+          const uint32_t w[3] = {ent.y, ent.z, ent.w};
+#pragma unroll
+          for (int wi = 0; wi < 3; ++wi) {
+#pragma unroll
+            for (int vi = 0; vi < 4; ++vi) {
+              const uint32_t d = leech_pair(w[wi], vi, l.x, l.y);
+#pragma unroll
+              for (int bb = 0; bb < B; ++bb)
+                acc[bb][wi] = dot2(d, xs[bb * npair + 12 * k + 4 * wi + vi], acc[bb][wi]);
+            }
+          }
+        }
+      }
+    }
     // epilogue: scale (with the 2^24 of the subnormal encoding), then the tail
     const float s = half_bits_to_float((uint16_t)g.scale) * 16777216.0f;
     const uint16_t* xh = (const uint16_t*)xs;
@@ -521,7 +559,10 @@ __device__ __forceinline__ uint2 stage_lut(int c, uint64_t entry) {
 // above batch 1, whose class extraction needs the registers, and the one-hot
 // mode, which keeps a block's four masks and its steps live across 12 pairs.)
 constexpr int leech_min_waves(int B, int BPL, int M) {
-  return M != kGain && M != kRot && M != kOneHot && !(M == kLp2 && B > 1) && B + BPL <= 4 ? 8 : 1;
+  return M != kGain && M != kRot && M != kOneHot && M != kLp2x && !(M == kLp2 && B > 1) &&
+                 B + BPL <= 4
+             ? 8
+             : 1;
 }
 
 // Stages s .. s + R - 1 of every sequence of the f32 buffer fb (the m
@@ -871,7 +912,7 @@ leech_gemv_kernel(MatSet ms, int rows, int nb, int tau, int cols, int nchunks, i
   // 3. the class table into LDS; the barrier also waits for x
   for (int c = tid; M != kDirect && c < LVQ_NUM_CLASSES; c += nthr) {
     const uint64_t e = c == tid ? te : table[c];
-    lut[c] = M == kLp2 ? stage_lut_lp2(e) : M == kOneHot ? stage_lut_onehot(e) : stage_lut(c, e);
+    lut[c] = is_lp2(M) ? stage_lut_lp2(e) : M == kOneHot ? stage_lut_onehot(e) : stage_lut(c, e);
   }
   __syncthreads();
   if (M == kRot) {
@@ -913,51 +954,6 @@ leech_gemv_kernel(MatSet ms, int rows, int nb, int tau, int cols, int nchunks, i
     decode_item<B, BPL, M>(ms, nb, tau, nchunks, kpad, rb, cb, lane, ib, lut, xs, xlane, acc);
   if (j + 2 < items)
     decode_item<B, BPL, M>(ms, nb, tau, nchunks, kpad, ra, ca, lane, ia, lut, xs, xlane, acc);
-}
-
-// LP2X side channel: after the LP2 kernel (whose records for these blocks are
-// zero), one wave per row adds the blocks LP2 cannot hold.  Lanes take the
-// row's entries in turn and decode them with the LP3 code words; the partial
-// sums are reduced in a fixed order and lane 63 adds s 2^24 times the total
-// to y.  Rows without entries return at once.
-template <int B>
-__global__ void __launch_bounds__(256)
-lp2x_exc_kernel(const uint64_t* __restrict__ table, const uint32_t* __restrict__ exc_off,
-                const uint4* __restrict__ exc, const uint16_t* __restrict__ scale, int rows,
-                int cols, const uint16_t* __restrict__ x, float* __restrict__ y) {
-  const int lane = threadIdx.x & (kWave - 1);
-  const int r = __builtin_amdgcn_readfirstlane((int)((blockIdx.x * blockDim.x + threadIdx.x) >> 6));
-  if (r >= rows) return;
-  const uint32_t e0 = exc_off[r], e1 = exc_off[r + 1];
-  if (e0 == e1) return;
-  float acc[B];
-#pragma unroll
-  for (int bb = 0; bb < B; ++bb) acc[bb] = 0.f;
-  for (uint32_t e = e0 + lane; e < e1; e += kWave) {
-    const uint4 ent = exc[e];
-    const int k = (int)(ent.x & 0xFFFFu);
-    const uint2 l = leech_lut(table[ent.x >> 16]);  // never class 0
-    const uint32_t w[3] = {ent.y, ent.z, ent.w};
-#pragma unroll
-    for (int wi = 0; wi < 3; ++wi) {
-#pragma unroll
-      for (int vi = 0; vi < 4; ++vi) {
-        const uint32_t d = leech_pair(w[wi], vi, l.x, l.y);
-        const int c = 24 * k + 8 * wi + 2 * vi;
-#pragma unroll
-        for (int bb = 0; bb < B; ++bb) {
-          const uint16_t* xr = x + (size_t)bb * cols + c;
-          acc[bb] = dot2(d, (uint32_t)xr[0] | ((uint32_t)xr[1] << 16), acc[bb]);
-        }
-      }
-    }
-  }
-  const float s = half_bits_to_float(scale[r]) * 16777216.0f;
-#pragma unroll
-  for (int bb = 0; bb < B; ++bb) {
-    const float tot = wave_sum_lane63(acc[bb]);
-    if (lane == kWave - 1) y[(size_t)bb * rows + r] += tot * s;
-  }
 }
 
 // Rows shorter than one block: y = sum of the unquantized tail only.
@@ -1090,6 +1086,7 @@ int launch_leech_bpl(const MatSet& ms, int mode, int rows, int cols, const uint1
     if (mode == kGain) return launch_leech_mode<B, BPL, kGain>(ms, rows, cols, x, st);
   }
   if (mode == kLp2) return launch_leech_mode<B, BPL, kLp2>(ms, rows, cols, x, st);
+  if (mode == kLp2x) return launch_leech_mode<B, BPL, kLp2x>(ms, rows, cols, x, st);
   if (mode == kDirect) return launch_leech_mode<B, BPL, kDirect>(ms, rows, cols, x, st);
   if (mode == kOneHot) return launch_leech_mode<B, BPL, kOneHot>(ms, rows, cols, x, st);
   if constexpr (gain_bpl_ok(B, BPL)) {
@@ -1163,7 +1160,8 @@ struct RotArgs {
 
 int single_gemv(const void* blob, int rows, int cols, const uint16_t* x, float* y, int batch,
                 void* stream, int mode, float gain0 = 1.f, float gain1 = 1.f,
-                const RotArgs& rot = RotArgs()) {
+                const RotArgs& rot = RotArgs(), const uint32_t* exc_off = nullptr,
+                const uint4* exc = nullptr) {
   if (rows < 0 || cols < 0) return LVQ_E_SHAPE;
   int e = check_batch(batch);
   if (e) return e;
@@ -1174,7 +1172,7 @@ int single_gemv(const void* blob, int rows, int cols, const uint16_t* x, float* 
   if (rows == 0) return LVQ_OK;
   if (cols == 0) return zero_output(y, (size_t)batch * rows, st);
   MatSet ms = {};
-  ms.v[0] = mode == kLp2      ? lp2_view(blob, (size_t)rows, (size_t)cols)
+  ms.v[0] = is_lp2(mode)     ? lp2_view(blob, (size_t)rows, (size_t)cols)
             : mode == kDirect ? direct_view(blob, (size_t)rows, (size_t)cols)
             : mode == kOneHot ? onehot_view(blob, (size_t)rows, (size_t)cols)
                               : leech_view(blob, (size_t)rows, (size_t)cols);
@@ -1183,6 +1181,8 @@ int single_gemv(const void* blob, int rows, int cols, const uint16_t* x, float* 
   for (int i = 1; i <= kMaxFused; ++i) ms.start[i] = rows;
   ms.gain[0] = gain0;
   ms.gain[1] = gain1;
+  ms.exc_off = exc_off;
+  ms.exc = exc;
   ms.rot_signs = rot.signs;
   ms.rot_q = rot.q;
   ms.rot_m = rot.m;
@@ -1234,25 +1234,14 @@ extern "C" int lvq_gemv_rotated(const void* blob, int rows, int cols, const uint
 
 extern "C" int lvq_gemv_lp2x(const void* blob, int rows, int cols, size_t n_exceptions,
                              const uint16_t* x, float* y, int batch, void* stream) {
-  int e = single_gemv(blob, rows, cols, x, y, batch, stream, kLp2);
-  if (e || rows <= 0 || cols < 24 || n_exceptions == 0) return e;
+  // without side-channel blocks the blob reads as plain LP2
+  if (n_exceptions == 0 || rows <= 0 || cols < 24)
+    return single_gemv(blob, rows, cols, x, y, batch, stream, kLp2);
+  if (!blob) return LVQ_E_NULL;
   const uint8_t* b = (const uint8_t*)blob;
-  const Sections s = lp2_sections((size_t)rows, (size_t)cols);
   const Lp2xSections sx = lp2x_sections((size_t)rows, (size_t)cols, n_exceptions);
-  const dim3 grid((unsigned)(((size_t)rows * kWave + 255) / 256)), wg(256);
-  const uint64_t* table = (const uint64_t*)(b + s.table);
-  const uint32_t* off = (const uint32_t*)(b + sx.exc_off);
-  const uint4* ex = (const uint4*)(b + sx.exc);
-  const uint16_t* scale = (const uint16_t*)(b + s.scale);
-  hipStream_t st = (hipStream_t)stream;
-  clear_hip_error();
-  switch (batch) {
-    case 1: hipLaunchKernelGGL(lp2x_exc_kernel<1>, grid, wg, 0, st, table, off, ex, scale, rows, cols, x, y); break;
-    case 2: hipLaunchKernelGGL(lp2x_exc_kernel<2>, grid, wg, 0, st, table, off, ex, scale, rows, cols, x, y); break;
-    case 3: hipLaunchKernelGGL(lp2x_exc_kernel<3>, grid, wg, 0, st, table, off, ex, scale, rows, cols, x, y); break;
-    default: hipLaunchKernelGGL(lp2x_exc_kernel<4>, grid, wg, 0, st, table, off, ex, scale, rows, cols, x, y); break;
-  }
-  return launch_status();
+  return single_gemv(blob, rows, cols, x, y, batch, stream, kLp2x, 1.f, 1.f, RotArgs(),
+                     (const uint32_t*)(b + sx.exc_off), (const uint4*)(b + sx.exc));
 }
 
 extern "C" int lvq_gemv_gain(const void* blob, int rows, int cols, float gain0, float gain1,
