@@ -203,3 +203,20 @@ def test_onehot_gemv_every_class():
     w = og.leech_weights(d["coords"], d["scale"], d["tail"], cols)
     y64, bound = og.gemv(w, x)
     assert og.check(y, y64, bound) <= 1.0
+
+
+def test_lp2x_without_side_channel_reads_as_lp2():
+    # shells 2..6 fit LP2 everywhere: no entries, and the LP2X blob's LP2 part
+    # is the LP2 blob, so the results are the LP2 kernel's bit for bit
+    rows, cols, batch = 300, 24 * 170 + 5, 3
+    d = synth.leech_matrix(rows, cols, 3, key=(rows, cols, 71))
+    blob, n_exc = lvq.expand_lp2x(d["coords"], d["scale"], d["tail"], rows, cols)
+    assert n_exc == 0
+    x = synth.activations(cols, batch, 3, key=(71,))
+    yx = empty((batch, rows), np.float32)
+    lvq.gemv_lp2x(to_dev(blob), rows, cols, 0, to_dev(x), yx, batch)
+    y2 = empty((batch, rows), np.float32)
+    lvq.gemv_lp2(to_dev(lvq.expand_lp2(d["coords"], d["scale"], d["tail"], rows, cols)), rows,
+                 cols, to_dev(x), y2, batch)
+    assert np.array_equal(to_host(yx, np.float32).view(np.uint32),
+                          to_host(y2, np.float32).view(np.uint32))
