@@ -178,7 +178,7 @@ def code_text(src):
 
 def kernel_sha():
     h = hashlib.sha256()
-    for f in ("lvq_gemv.hip", "common.h", "layout.h"):
+    for f in ("lvq_gemv.hip", "common.h", "layout.h", "rotate_dev.h"):
         src = open(os.path.join(ROOT, "dequant_gemv_lvq_amd", "csrc", f)).read()
         h.update(code_text(src).encode())
     return h.hexdigest()[:16]

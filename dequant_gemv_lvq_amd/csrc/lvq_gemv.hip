@@ -917,7 +917,6 @@ leech_gemv_kernel(MatSet ms, int rows, int nb, int tau, int cols, int nchunks, i
   __syncthreads();
   if (M == kRot) {
     // the first items' weight loads stay in flight meanwhile
-#pragma unroll
     for (int bb = 0; bb < B; ++bb)
       rotate_x_lds((uint16_t*)xs + (size_t)bb * kpad, fb, qs, sw, ms, cols, tid, nthr);
   }

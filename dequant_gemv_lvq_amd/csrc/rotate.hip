@@ -175,7 +175,8 @@ rotate_kernel(const uint16_t* x, const uint32_t* __restrict__ signs,
     }
     // stages 0-2 in registers
 #pragma unroll
-    for (int h = 1; h < 8; h <<= 1) {
+    for (int e = 0; e < 3; ++e) {
+      const int h = 1 << e;
       if (h >= cw) break;
 #pragma unroll
       for (int t = 0; t < 8; ++t) {

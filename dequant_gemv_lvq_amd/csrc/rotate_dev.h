@@ -35,7 +35,8 @@ __device__ __forceinline__ uint16_t rot_out(float v, float scale) {
 // Stages 0-2 of 8 values in registers, in the order h = 1, 2, 4.
 __device__ __forceinline__ void rot_reg_stages(float (&v)[8], int cw) {
 #pragma unroll
-  for (int h = 1; h < 8; h <<= 1) {
+  for (int e = 0; e < 3; ++e) {
+    const int h = 1 << e;
     if (h >= cw) break;
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
@@ -60,7 +61,8 @@ template <int R>
 __device__ __forceinline__ void rot_set_stages(float (&v)[1 << R]) {
   constexpr int kR = 1 << R;
 #pragma unroll
-  for (int h = 1; h < kR; h <<= 1) {
+  for (int e = 0; e < R; ++e) {
+    const int h = 1 << e;
 #pragma unroll
     for (int t = 0; t < kR; ++t) {
       if (t & h) continue;
