@@ -15,18 +15,20 @@
 //
 // gfx950 design.  The m interleaved sequences are independent once Q has mixed
 // each group, so one workgroup takes one (batch row, b) pair and one K-point
-// transform (K <= 32768).  A lane produces 8 consecutive values of its
-// sequence: for m = 1 one 16-byte load of x, for m > 1 the Q mix
-// w[c] = sum_d Q[b][d] x'[c m + d] from the row of x staged in LDS with row b
-// of Q in scalar registers; the signs are XORed into the fp16 sign bits
-// (exact).  Butterfly stages 0-2 run in the lane's registers, stages 3-8
-// across the 64 lanes of its wave by lane exchanges, so a wave finishes
-// 512-point transforms without touching LDS.  For K <= 512 the results are
-// scaled, rounded to fp16 and stored from registers.  Otherwise they go to
-// LDS once (f32), and after one barrier a single pass does the remaining
-// stages 9 .. log2 K - 1 (up to 64 values per thread, coordinates 512 apart,
-// consecutive threads at consecutive addresses: no bank conflicts) and
-// stores.  LDS: 4 K bytes (+ 2 n for the staged x when m > 1); the largest
+// transform (K <= 32768); the signs are XORed into the fp16 sign bits as x
+// arrives (exact).  Two kernels, which apply every stage's butterflies to the
+// same operands in the same order and so give the same bits:
+// - K >= 16 and m <= 8 (rotate16_kernel, every Qwen3-family width but the
+//   wide ones): a thread takes 16 consecutive values of its sequence, forms
+//   their Q mix in registers straight from global memory, runs stages 0-3 in
+//   registers, and radix passes over an f32 copy in LDS do the rest.
+// - m > 8 or K < 16 (rotate_kernel): the row of x is staged in LDS, each
+//   thread forms one output of the Q mix into an f32 sequence in LDS, then
+//   stages 0-3 with 16 consecutive values per thread and radix passes; for
+//   K < 16 one lane holds the whole sequence.
+// The passes for stages 4 and up have consecutive threads on consecutive
+// addresses (no bank conflicts) and one barrier each; the last one scales,
+// rounds to fp16 and stores.  LDS: 4 K bytes (+ 2 n where x is staged); the widest
 // Qwen3-family width, 25600 (the one that did not fit the pages' card as
 // f32), takes 54 KiB.
 
@@ -37,10 +39,6 @@ namespace lvq {
 
 constexpr int kRotThreads = 1024;
 constexpr int kRotMaxM = 32;
-
-
-
-
 
 // Stages s .. s + R - 1 over buf: coordinates 2^s apart, consecutive threads
 // at consecutive addresses (for s >= 4).  The last pass scales, rounds and
@@ -76,7 +74,8 @@ __device__ __forceinline__ void rot_high_pass(float* buf, int k, int s, bool las
   }
 }
 
-// Workgroup (b, batch row): y[c m + b] for c < K.
+// Workgroup (b, batch row): y[c m + b] for c < K, for the shapes the 16-value
+// kernel below does not take: m > 8, and K < 16.
 template <int MMAX>
 __global__ void __launch_bounds__(kRotThreads)
 rotate_kernel(const uint16_t* x, const uint32_t* __restrict__ signs,
@@ -84,13 +83,13 @@ rotate_kernel(const uint16_t* x, const uint32_t* __restrict__ signs,
   // y may be x when m = 1: a row's one workgroup reads all of it before its
   // barrier and writes after it (for m > 1 the host refuses overlap)
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  const int tid = threadIdx.x, nthr = blockDim.x, lane = tid & (kWave - 1);
+  const int tid = threadIdx.x, nthr = blockDim.x;
   const int b = MMAX == 1 ? 0 : blockIdx.x;
   const int mm = MMAX == 1 ? 1 : m;
   const int k = n / mm;
   const uint16_t* xr = x + (size_t)blockIdx.y * n;
   uint16_t* yr = y + (size_t)blockIdx.y * n;
-  // LDS: the staged row of x (m > 1), then the f32 sequence (K > 512)
+  // LDS (m > 1): the staged row of x, then the f32 sequence
   uint16_t* xs = (uint16_t*)smem;
   float* buf = (float*)(smem + (MMAX > 1 ? (((size_t)n * 2 + 15) & ~(size_t)15) : 0));
   if (MMAX == 1 && q) scale *= q[0];  // a 1 x 1 Q is a scale (+-1 when orthogonal)
@@ -117,8 +116,7 @@ rotate_kernel(const uint16_t* x, const uint32_t* __restrict__ signs,
         }
       }
     } else {
-      for (int j = tid; j < n; j += nthr)
-        xs[j] = xr[j] ^ (signs ? (uint16_t)(((signs[j >> 5] >> (j & 31)) & 1u) << 15) : 0);
+      for (int j = tid; j < n; j += nthr) xs[j] = xr[j] ^ rot_sign_bit(signs, j);
     }
     // row b of Q: uniform, so scalar loads
     float qrow[MMAX];
@@ -134,96 +132,56 @@ rotate_kernel(const uint16_t* x, const uint32_t* __restrict__ signs,
       buf[c] = a;
     }
     __syncthreads();
-  }
-
-  // 1. 8 consecutive values per lane (fewer when K < 8), stages 0 .. 8
-  const int cw = k < 8 ? k : 8;              // values per lane
-  const int nch = k / cw;                    // lanes with values
-  const int lo_bits = logk < 9 ? logk : 9;   // stages done before LDS
-  for (int ch0 = 0; ch0 < nch; ch0 += nthr) {
-    const int ch = ch0 + tid;
-    float v[8];
-    if (MMAX == 1) {
-      if (cw == 8) {
-        uint4 u = ch < nch ? *(const uint4*)(xr + (size_t)ch * 8) : make_uint4(0, 0, 0, 0);
-        const uint32_t s8 = signs && ch < nch ? signs[ch >> 2] >> ((ch & 3) * 8) : 0u;
-        u = rot_apply_signs(u, s8);
-        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+    if (logk >= 4) {  // uniform
+      // stages 0-3 with 16 consecutive values per thread (16-byte LDS
+      // accesses), then radix passes with consecutive threads on consecutive
+      // addresses: a barrier per pass, no lane exchanges
+      for (int set = tid; set < (k >> 4); set += nthr) {
+        float v[16];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          v[2 * i] = rot_half((uint16_t)w[i]);
-          v[2 * i + 1] = rot_half((uint16_t)(w[i] >> 16));
+          const float4 f = *(const float4*)(buf + 16 * set + 4 * i);
+          v[4 * i] = f.x; v[4 * i + 1] = f.y; v[4 * i + 2] = f.z; v[4 * i + 3] = f.w;
         }
-      } else {
+        rot_set_stages<4>(v);
+        if (logk == 4) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const int j = ch * cw + i;
-          v[i] = 0.f;
-          if (i < cw && ch < nch)
-            v[i] = rot_half(xr[j] ^ (signs ? (uint16_t)(((signs[j >> 5] >> (j & 31)) & 1u) << 15)
-                                           : 0));
-        }
-      }
-    } else if (cw == 8) {
-      const float4 lo = ch < nch ? *(const float4*)(buf + ch * 8) : make_float4(0, 0, 0, 0);
-      const float4 hi = ch < nch ? *(const float4*)(buf + ch * 8 + 4) : make_float4(0, 0, 0, 0);
-      v[0] = lo.x; v[1] = lo.y; v[2] = lo.z; v[3] = lo.w;
-      v[4] = hi.x; v[5] = hi.y; v[6] = hi.z; v[7] = hi.w;
-    } else {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) v[i] = i < cw && ch < nch ? buf[ch * cw + i] : 0.f;
-    }
-    // stages 0-2 in registers
-#pragma unroll
-    for (int e = 0; e < 3; ++e) {
-      const int h = 1 << e;
-      if (h >= cw) break;
-#pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        if (t & h) continue;
-        const float lo = v[t], hi = v[t + h];
-        v[t] = lo + hi;
-        v[t + h] = lo - hi;
-      }
-    }
-    // stages 3 .. lo_bits - 1 across lanes (lane bit j = chunk bit j)
-    for (int j = 0; (8 << j) <= (1 << lo_bits) && cw == 8; ++j) {
-      if ((8 << j) == (1 << lo_bits)) break;
-#pragma unroll
-      for (int t = 0; t < 8; ++t) v[t] = rot_lane_bfly(v[t], 1 << j, lane);
-    }
-    if (ch < nch) {
-      if (logk <= 9) {
-        if (MMAX == 1 && cw == 8) {
-          uint32_t w[4];
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            w[i] = rot_out(v[2 * i], scale) | ((uint32_t)rot_out(v[2 * i + 1], scale) << 16);
-          *(uint4*)(yr + (size_t)ch * 8) = make_uint4(w[0], w[1], w[2], w[3]);
+          for (int t = 0; t < 16; ++t) yr[(size_t)(16 * set + t) * mm + b] = rot_out(v[t], scale);
         } else {
 #pragma unroll
-          for (int i = 0; i < 8; ++i)
-            if (i < cw) yr[(size_t)(ch * cw + i) * mm + b] = rot_out(v[i], scale);
+          for (int i = 0; i < 4; ++i)
+            *(float4*)(buf + 16 * set + 4 * i) =
+                make_float4(v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]);
         }
-      } else {
-        *(float4*)(buf + ch * 8) = make_float4(v[0], v[1], v[2], v[3]);
-        *(float4*)(buf + ch * 8 + 4) = make_float4(v[4], v[5], v[6], v[7]);
       }
+      for (int s = 4; s < logk; s += 4) {
+        __syncthreads();
+        const int r = logk - s < 4 ? logk - s : 4;
+        const bool last = s + r == logk;
+        if (r == 4) rot_high_pass<4>(buf, k, s, last, mm, b, scale, yr, tid, nthr);
+        else if (r == 3) rot_high_pass<3>(buf, k, s, last, mm, b, scale, yr, tid, nthr);
+        else if (r == 2) rot_high_pass<2>(buf, k, s, last, mm, b, scale, yr, tid, nthr);
+        else rot_high_pass<1>(buf, k, s, last, mm, b, scale, yr, tid, nthr);
+      }
+      return;
     }
   }
-  if (logk <= 9) return;  // uniform
-  __syncthreads();
 
-  // 2. stages 9 .. log2 K - 1, up to four per pass; the last pass scales,
-  //    rounds and stores
-  for (int s = 9; s < logk; s += 4) {
-    const int r = logk - s < 4 ? logk - s : 4;
-    const bool last = s + r == logk;
-    if (r == 4) rot_high_pass<4>(buf, k, s, last, mm, b, scale, yr, tid, nthr);
-    else if (r == 3) rot_high_pass<3>(buf, k, s, last, mm, b, scale, yr, tid, nthr);
-    else if (r == 2) rot_high_pass<2>(buf, k, s, last, mm, b, scale, yr, tid, nthr);
-    else rot_high_pass<1>(buf, k, s, last, mm, b, scale, yr, tid, nthr);
-    if (!last) __syncthreads();
+  // K < 16: one lane holds the whole sequence (K <= 8 values) and runs every
+  // stage in its registers (m = 1 reads x itself, with the signs; m > 1 the
+  // Q mix)
+  if (tid == 0) {
+    float v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      v[i] = 0.f;
+      if (i < k)
+        v[i] = MMAX == 1 ? rot_half(xr[i] ^ rot_sign_bit(signs, i)) : buf[i];
+    }
+    rot_reg_stages(v, k);
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      if (i < k) yr[(size_t)i * mm + b] = rot_out(v[i], scale);
   }
 }
 
@@ -358,17 +316,11 @@ int launch_rotate(const uint16_t* x, const uint32_t* signs, const float* q, int 
   int logk = 0;
   while ((1 << logk) < k) ++logk;
   if (logk > 15) return LVQ_E_SHAPE;
-  const size_t lds = (MMAX > 1 ? (((size_t)n * 2 + 15) & ~(size_t)15) + (size_t)k * 4
-                               : (logk > 9 ? (size_t)k * 4 : 0));
+  if (MMAX == 1 && k >= 16) return LVQ_E_SHAPE;  // the 16-value kernel's
+  const size_t lds = MMAX > 1 ? (((size_t)n * 2 + 15) & ~(size_t)15) + (size_t)k * 4 : 0;
   if (lds > device_lds_bytes()) return LVQ_E_SHAPE;
-  // one lane per 8 values (and for m > 1 enough to stage x), whole waves
-  const int cw = k < 8 ? k : 8;
-  int want = k / cw;
-  if (MMAX > 1 && k > want) want = k;
-  if (logk > 9 && (k >> (logk - 9 < 4 ? logk - 9 : 4)) > want)
-    want = k >> (logk - 9 < 4 ? logk - 9 : 4);
-  int threads = (want + kWave - 1) / kWave * kWave;
-  if (threads < kWave) threads = kWave;
+  // m > 1: one thread per Q-mix output (whole waves); m = 1 (K < 16): one wave
+  int threads = MMAX > 1 ? (k + kWave - 1) / kWave * kWave : kWave;
   if (threads > kRotThreads) threads = kRotThreads;
   const float scale = (float)(1.0 / __builtin_sqrt((double)k));
   clear_hip_error();

@@ -22,12 +22,6 @@ __device__ __forceinline__ uint16_t rot_sign_bit(const uint32_t* signs, int j) {
   return signs ? (uint16_t)(((signs[j >> 5] >> (j & 31)) & 1u) << 15) : (uint16_t)0;
 }
 
-// Butterfly over lane bit `mask`: the lower lane keeps a + b, the upper b' = a - b.
-__device__ __forceinline__ float rot_lane_bfly(float v, int mask, int lane) {
-  const float o = __shfl_xor(v, mask, kWave);
-  return (lane & mask) ? o - v : v + o;
-}
-
 __device__ __forceinline__ uint16_t rot_out(float v, float scale) {
   return __builtin_bit_cast(uint16_t, (_Float16)(v * scale));
 }
@@ -45,14 +39,6 @@ __device__ __forceinline__ void rot_reg_stages(float (&v)[8], int cw) {
       v[t] = lo + hi;
       v[t + h] = lo - hi;
     }
-  }
-}
-
-// Stages 3 .. lo_bits - 1 across the lanes of a wave (lane bit j = chunk bit j).
-__device__ __forceinline__ void rot_lane_stages(float (&v)[8], int cw, int lo_bits, int lane) {
-  for (int j = 0; cw == 8 && (8 << j) < (1 << lo_bits); ++j) {
-#pragma unroll
-    for (int t = 0; t < 8; ++t) v[t] = rot_lane_bfly(v[t], 1 << j, lane);
   }
 }
 
