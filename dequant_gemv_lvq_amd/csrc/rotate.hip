@@ -124,12 +124,39 @@ rotate_kernel(const uint16_t* x, const uint32_t* __restrict__ signs,
     for (int d = 0; d < MMAX; ++d)
       qrow[d] = d < m ? (q ? q[b * m + d] : (d == b ? 1.f : 0.f)) : 0.f;
     __syncthreads();
-    for (int c = tid; c < k; c += nthr) {
-      float a = 0.f;
+    if (MMAX > 8) {
+      // wide groups: a lane reads its group as aligned words (one more than
+      // half of MMAX), shifts each pair of halves into place by its own
+      // parity, and runs all MMAX terms, those past m masked to +0 (with q 0
+      // adding +0 leaves the sum as it is): no branch per term, every read in
+      // flight at once.  The reads past the group stay inside the LDS
+      // allocation (the host adds 64 bytes after the f32 sequence).
+      const uint32_t* xs32 = (const uint32_t*)xs;
+      for (int c = tid; c < k; c += nthr) {
+        const int h0 = c * m;
+        const int w0 = h0 >> 1;
+        const uint32_t sh = (uint32_t)(h0 & 1) * 16;
+        uint32_t dw[MMAX / 2 + 1];
 #pragma unroll
-      for (int d = 0; d < MMAX; ++d)
-        if (d < m) a = __builtin_fmaf(qrow[d], rot_half(xs[c * m + d]), a);
-      buf[c] = a;
+        for (int j = 0; j <= MMAX / 2; ++j) dw[j] = xs32[w0 + j];
+        float a = 0.f;
+#pragma unroll
+        for (int j = 0; j < MMAX / 2; ++j) {
+          const uint32_t keep = 2 * j + 1 < m ? 0xFFFFFFFFu : 2 * j < m ? 0xFFFFu : 0u;  // uniform
+          const uint32_t pr = __builtin_amdgcn_alignbit(dw[j + 1], dw[j], sh) & keep;
+          a = __builtin_fmaf(qrow[2 * j], rot_half((uint16_t)pr), a);
+          a = __builtin_fmaf(qrow[2 * j + 1], rot_half((uint16_t)(pr >> 16)), a);
+        }
+        buf[c] = a;
+      }
+    } else {
+      for (int c = tid; c < k; c += nthr) {
+        float a = 0.f;
+#pragma unroll
+        for (int d = 0; d < MMAX; ++d)
+          if (d < m) a = __builtin_fmaf(qrow[d], rot_half(xs[c * m + d]), a);
+        buf[c] = a;
+      }
     }
     __syncthreads();
     if (logk >= 4) {  // uniform
@@ -317,7 +344,9 @@ int launch_rotate(const uint16_t* x, const uint32_t* signs, const float* q, int 
   while ((1 << logk) < k) ++logk;
   if (logk > 15) return LVQ_E_SHAPE;
   if (MMAX == 1 && k >= 16) return LVQ_E_SHAPE;  // the 16-value kernel's
-  const size_t lds = MMAX > 1 ? (((size_t)n * 2 + 15) & ~(size_t)15) + (size_t)k * 4 : 0;
+  // m > 8: 64 bytes after the f32 sequence for the Q mix's reads past x
+  const size_t lds =
+      MMAX > 1 ? (((size_t)n * 2 + 15) & ~(size_t)15) + (size_t)k * 4 + (MMAX > 8 ? 64 : 0) : 0;
   if (lds > device_lds_bytes()) return LVQ_E_SHAPE;
   // m > 1: one thread per Q-mix output (whole waves); m = 1 (K < 16): one wave
   int threads = MMAX > 1 ? (k + kWave - 1) / kWave * kWave : kWave;
