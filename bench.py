@@ -294,6 +294,7 @@ class Bench:
 
     # one Leech matrix at one shape and batch
     def leech(self, cfg, rows, cols, batch, d=None, keep=False):
+        import numpy as np
         import synth
         torch, lvq = self.torch, self.lvq
         if d is None:
@@ -315,6 +316,14 @@ class Bench:
         out = (rec, d, x, yd.cpu().numpy()) if keep else rec
         if keep:
             self.graph_us = self.graph(lambda i: lvq.gemv(bufs[i % n], rows, cols, xd, yd, batch))
+            # the bit-exact gate: the timed blob decodes to the input points on
+            # the GPU, and they re-expand to the same blob
+            dec = torch.empty((rows, cols // 24, 24), dtype=torch.int8, device="cuda")
+            lvq.decode(bufs[0], rows, cols, dec)
+            got = dec.cpu().numpy()
+            rec["bitexact"] = bool(np.array_equal(got, d["coords"]) and np.array_equal(
+                lvq.expand(got, d["scale"], d["tail"], rows, cols), blob))
+            del dec
         del bufs
         torch.cuda.empty_cache()
         return out
@@ -874,6 +883,9 @@ def main():
         cpu, ratio = cpu_baseline(d, x, y_timed, [(1, 1536, 1536), (3, 4096, 4096),
                                                   (3, 12288, 4096), (3, 1024, 4096)])
         head["parity_max_ratio"] = round(ratio, 5)
+        head["oracle_us_1core"] = cpu["oracle_us_1core"]
+        head["oracle_us_ncores"] = cpu["oracle_us_ncores"]
+        head["ncores"] = cpu["cores"]
         log("cpu baseline done in %.1fs" % (time.perf_counter() - t0))
 
     us = head["us_median"]
