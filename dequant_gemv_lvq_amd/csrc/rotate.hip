@@ -5,10 +5,12 @@
 // transform that needs the whole activation resident in one block's shared
 // memory (served-path setup, and the section on the rotated basis and the
 // shared-memory wall: the widest activation of the largest model needed
-// 102,400 B of f32 and did not fit that card).  The Tetra summary (section
-// "What the kernel does per token") gives the form for widths that are not
-// powers of two: (H kron Q)(S x), S random signs, H a power-of-two
-// Walsh-Hadamard transform, Q a small orthogonal matrix.
+// 102,400 B of f32 and did not fit that card).  That fixes the power-of-two
+// case (m = 1).  Widths that are not powers of two borrow the form another
+// system uses: the blog post "Qwen3.8-27B on a 12 GB card" (section "What the
+// kernel does per token") gives Mirai S's runtime rotation as (H kron Q)(S x),
+// S random signs, H a power-of-two Walsh-Hadamard transform, Q a small
+// orthogonal matrix.
 //
 // n = K m, K a power of two, coordinate a m + b; H = K^-1/2 times the Sylvester
 // matrix ((-1)^popcount(a & c)); Q is m x m (identity when none is given).

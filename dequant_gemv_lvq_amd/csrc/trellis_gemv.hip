@@ -1,11 +1,12 @@
 // Bitshift-trellis matvec (trellis_gemv), the trellis comparison arm.
 //
 // Source: blog "Qwen3.8-27B on a 12 GB card", section "A trellis is a codebook
-// you walk": the state is the last L bits of the stream, each step shifts T
-// new bits in, so decoding a position means reading one L-bit window and no
-// step depends on the previous step's output.  Here L = 16, T = 2, one weight
-// per step, a 65536-entry fp16 table and one scale per row; every 256 columns
-// form a tail-biting packet.
+// you walk".  A position's decoder state is a fixed-width window of the code
+// stream ending at that position's symbol, so each weight is one window read
+// plus one table entry, and positions decode independently of each other.
+// Here the window is 16 bits, a symbol 2 bits (one weight per symbol), the
+// table holds 65536 fp16 values, each row has one scale, and each run of 256
+// columns is a tail-biting packet.
 //
 // gfx950 design.  One 1024-thread workgroup per CU copies the 128 KiB table
 // and x into LDS with buffer loads that write LDS directly, then its waves

@@ -21,9 +21,10 @@ Arms and their sources:
            one 2-bit code that is peeled low bits first.  Reading: bit_i is bit
            i of that code; coeffs are fp16 [groups, 3, out].
   trellis  blog "Qwen3.8-27B on a 12 GB card", section "A trellis is a codebook
-           you walk": the state is the last L bits of the stream, each step
-           shifts T new bits in and emits V weights.  Here L=16, T=2, V=1; a
-           weight is s_r * table[state]; packets restart every 256 columns.
+           you walk": a position's state is the L-bit window of the code
+           stream that ends at its symbol (T bits per symbol, V weights per
+           symbol).  Here L=16, T=2, V=1; a weight is s_r * table[state];
+           packets restart every 256 columns.
            Readings (parity unpinned beyond the pins listed in the tests):
            symbols are read MSB-first within each 32-bit word, and a packet is
            tail-biting (the 7 symbols before symbol 0 are the packet's last 7).

@@ -2,13 +2,17 @@
 
 Sources.  arXiv 2609.02652 keeps the weights in an incoherence-rotated basis,
 so every projection first applies a Walsh-Hadamard transform to its input
-activation, and the paper's kernel holds the whole activation in shared memory
-(setup paragraph of the served-path section, and the section on the rotated
-basis and the shared-memory wall).  The Tetra summary (arXiv 2609.35465, the
-"What the kernel does per token" section) spells the runtime rotation out for
-widths that are not powers of two: x_rot = (H kron Q)(S x), with S random
-signs, H a power-of-two Walsh-Hadamard transform and Q a small orthogonal
-matrix (5 x 5 for 5120 = 5 x 1024, 3 x 3 for 6144 = 3 x 2048).
+activation, held whole in one thread block's shared memory (setup paragraph
+of the served-path section, and the paragraph on the rotated basis and the
+shared-memory wall).  That fixes the power-of-two case only: one
+Walsh-Hadamard transform over the whole input (m = 1 below).  For widths that
+are not powers of two (9,728, 17,408 and 25,600 in the Qwen3 family) this
+module borrows the form of another system: the blog post "Qwen3.8-27B on a
+12 GB card" (section "What the kernel does per token") gives the runtime
+rotation of Mirai S, a QTIP-style trellis model, as x_rot = (H kron Q)(S x),
+with S random signs, H a 1024- or 2048-point Walsh-Hadamard transform and Q
+a small orthogonal matrix (5 x 5 for 5120 = 5 x 1024, 3 x 3 for
+6144 = 3 x 2048).  The paper names none of S, Q or that factorisation.
 
 Reading (the pages fix neither the normalisation nor the index order):
   n = K * m with K a power of two; coordinate i = a * m + b (a < K, b < m);
