@@ -17,6 +17,7 @@ LIB_PATH = os.path.join(_HERE, "liblvq.so")
 
 NUM_CLASSES = 302
 STREAM_SINK_WORDS = 4096
+STREAM_GEOM_SINK_WORDS = 65536
 MAX_FUSED = 4
 MAX_BATCH = 4
 
@@ -85,6 +86,7 @@ def _load():
         "lvq_rotate": (i, [vp, vp, vp, i, i, vp, i, vp]),
         "lvq_gemv_rotated": (i, [vp, i, i, vp, vp, i, vp, vp, i, vp]),
         "lvq_stream_read": (i, [vp, sz, vp, vp]),
+        "lvq_stream_read_geom": (i, [vp, sz, vp, i, i, i, i, vp]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -102,7 +104,7 @@ EXPORTED = ("lvq_strerror", "lvq_last_error_index", "lvq_class_table", "lvq_layo
             "lvq_rank", "lvq_gemv", "lvq_gemv_gain",
             "lvq_unfold", "lvq_gemv_fused", "lvq_gemv_noweights", "lvq_decode",
             "bpdq_gemv", "trellis_gemv", "fp16_gemv", "lvq_rotate", "lvq_gemv_rotated",
-            "lvq_stream_read")
+            "lvq_stream_read", "lvq_stream_read_geom")
 
 
 def library():
@@ -159,20 +161,30 @@ def layout_bytes(rows: int, cols: int) -> int:
     return int(_lib.lvq_layout_bytes(int(rows), int(cols)))
 
 
-def expand(coords, scale, tail, rows: int, cols: int) -> np.ndarray:
-    """Host expansion: coords int8 [rows][cols//24][24], scale/tail fp16 bits
-    (uint16) -> packed blob (uint8, lvq_layout_bytes long)."""
+def _host_inputs(coords, scale, tail, rows: int, cols: int):
+    """The host expanders' inputs as contiguous arrays of the exact sizes the
+    C expanders read (coords int8 rows*(cols//24)*24, scale uint16 rows, tail
+    uint16 rows*(cols%24) or None when cols%24 == 0); LvqError(LVQ_E_SHAPE)
+    otherwise, before any native call, so a short array is never read past."""
+    if rows < 0 or cols < 0:
+        _check(LVQ_E_SHAPE)
     coords = np.ascontiguousarray(coords, dtype=np.int8)
     scale = np.ascontiguousarray(scale, dtype=np.uint16)
     tau = cols % 24
-    tail = None if tau == 0 else np.ascontiguousarray(tail, dtype=np.uint16)
-    n = _lib.lvq_layout_bytes(int(rows), int(cols))
-    if rows < 0 or cols < 0:
+    if tau and tail is None:
         _check(LVQ_E_SHAPE)
+    tail = None if tau == 0 else np.ascontiguousarray(tail, dtype=np.uint16)
     if coords.size != rows * (cols // 24) * 24 or scale.size != rows or (
             tail is not None and tail.size != rows * tau):
         _check(LVQ_E_SHAPE)
-    blob = np.empty(n, dtype=np.uint8)
+    return coords, scale, tail
+
+
+def expand(coords, scale, tail, rows: int, cols: int) -> np.ndarray:
+    """Host expansion: coords int8 [rows][cols//24][24], scale/tail fp16 bits
+    (uint16) -> packed blob (uint8, lvq_layout_bytes long)."""
+    coords, scale, tail = _host_inputs(coords, scale, tail, rows, cols)
+    blob = np.empty(_lib.lvq_layout_bytes(int(rows), int(cols)), dtype=np.uint8)
     code = _lib.lvq_expand(_ptr(coords), _ptr(scale), _ptr(tail), int(rows), int(cols),
                            blob.ctypes.data)
     if code != LVQ_OK:
@@ -188,12 +200,7 @@ def layout_bytes_lp2(rows: int, cols: int) -> int:
 
 def expand_lp2(coords, scale, tail, rows: int, cols: int) -> np.ndarray:
     """Host expansion into the LP2 layout (two rank planes, class in the record)."""
-    coords = np.ascontiguousarray(coords, dtype=np.int8)
-    scale = np.ascontiguousarray(scale, dtype=np.uint16)
-    tau = cols % 24
-    tail = None if tau == 0 else np.ascontiguousarray(tail, dtype=np.uint16)
-    if rows < 0 or cols < 0 or coords.size != rows * (cols // 24) * 24:
-        _check(LVQ_E_SHAPE)
+    coords, scale, tail = _host_inputs(coords, scale, tail, rows, cols)
     blob = np.empty(_lib.lvq_layout_bytes_lp2(int(rows), int(cols)), dtype=np.uint8)
     code = _lib.lvq_expand_lp2(_ptr(coords), _ptr(scale), _ptr(tail), int(rows), int(cols),
                                blob.ctypes.data)
@@ -225,12 +232,7 @@ def expand_direct(coords, scale, tail, rows: int, cols: int) -> np.ndarray:
 
 
 def _expand_with(expand, nbytes, coords, scale, tail, rows: int, cols: int) -> np.ndarray:
-    coords = np.ascontiguousarray(coords, dtype=np.int8)
-    scale = np.ascontiguousarray(scale, dtype=np.uint16)
-    tau = cols % 24
-    tail = None if tau == 0 else np.ascontiguousarray(tail, dtype=np.uint16)
-    if rows < 0 or cols < 0 or coords.size != rows * (cols // 24) * 24:
-        _check(LVQ_E_SHAPE)
+    coords, scale, tail = _host_inputs(coords, scale, tail, rows, cols)
     blob = np.empty(nbytes(int(rows), int(cols)), dtype=np.uint8)
     code = expand(_ptr(coords), _ptr(scale), _ptr(tail), int(rows), int(cols), blob.ctypes.data)
     if code != LVQ_OK:
@@ -242,12 +244,7 @@ def _expand_with(expand, nbytes, coords, scale, tail, rows: int, cols: int) -> n
 
 def expand_lp2x(coords, scale, tail, rows: int, cols: int) -> tuple:
     """Host expansion into LP2X; returns (blob, number of side-channel blocks)."""
-    coords = np.ascontiguousarray(coords, dtype=np.int8)
-    scale = np.ascontiguousarray(scale, dtype=np.uint16)
-    tau = cols % 24
-    tail = None if tau == 0 else np.ascontiguousarray(tail, dtype=np.uint16)
-    if rows < 0 or cols < 0 or coords.size != rows * (cols // 24) * 24:
-        _check(LVQ_E_SHAPE)
+    coords, scale, tail = _host_inputs(coords, scale, tail, rows, cols)
     n = ctypes.c_size_t()
     code = _lib.lvq_lp2x_exceptions(_ptr(coords), int(rows), int(cols), ctypes.byref(n))
     if code == LVQ_OK:
@@ -263,12 +260,9 @@ def expand_lp2x(coords, scale, tail, rows: int, cols: int) -> tuple:
 
 def expand_gain(coords, gain_bits, scale, tail, rows: int, cols: int) -> np.ndarray:
     """lvq_expand with a shape-gain bit per block (uint8 [rows][cols//24])."""
-    coords = np.ascontiguousarray(coords, dtype=np.int8)
+    coords, scale, tail = _host_inputs(coords, scale, tail, rows, cols)
     gain_bits = np.ascontiguousarray(gain_bits, dtype=np.uint8)
-    scale = np.ascontiguousarray(scale, dtype=np.uint16)
-    tau = cols % 24
-    tail = None if tau == 0 else np.ascontiguousarray(tail, dtype=np.uint16)
-    if rows < 0 or cols < 0 or gain_bits.size != rows * (cols // 24):
+    if gain_bits.size != rows * (cols // 24):
         _check(LVQ_E_SHAPE)
     blob = np.empty(_lib.lvq_layout_bytes(int(rows), int(cols)), dtype=np.uint8)
     code = _lib.lvq_expand_gain(_ptr(coords), _ptr(gain_bits), _ptr(scale), _ptr(tail),
@@ -391,3 +385,14 @@ def stream_read(buf, nbytes: int, sink, stream=None):
     """Measurement hook: read nbytes of buf once; the XOR of the STREAM_SINK_WORDS
     words of sink (cleared by the caller) is the XOR of the buffer's words."""
     _check(_lib.lvq_stream_read(_ptr(buf), int(nbytes), _ptr(sink), _stream(stream)))
+
+
+def stream_read_geom(buf, nbytes: int, sink, threads: int, wgs_per_cu: int, unroll: int,
+                     nontemporal: bool, stream=None):
+    """Measurement hook: the read of stream_read with the launch shape given
+    (threads per workgroup, workgroups per CU or 0 for one trip per thread,
+    16-byte loads in flight per thread, non-temporal loads or not); sink has
+    STREAM_GEOM_SINK_WORDS words, cleared by the caller."""
+    _check(_lib.lvq_stream_read_geom(_ptr(buf), int(nbytes), _ptr(sink), int(threads),
+                                     int(wgs_per_cu), int(unroll), int(bool(nontemporal)),
+                                     _stream(stream)))

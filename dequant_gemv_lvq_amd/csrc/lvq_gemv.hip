@@ -6,12 +6,12 @@
 // epilogue, lvq_gemv_direct, lvq_gemv_onehot), the rotation in the prologue
 // (lvq_gemv_rotated), and the lvq_decode test hook.
 //
-// Source: arXiv 2609.02652, section 1, contribution C1: a fused kernel reads
-// the unfolded layout with shifts, masks and a predicated table lookup, the
-// same instruction sequence on every lane whatever the class, and the
-// combinatorial index is never decoded inside the matvec.  The Tetra summary
-// (arXiv 2609.35465, section 5.1) adds the epilogue: apply the row scale, then
-// add the unquantized tail.
+// Source: arXiv 2609.02652, section 1, contribution C1 (the fused multi-shell
+// decoder): the matvec decodes an offline-expanded layout with bit operations
+// and one table read per block, with no branch that depends on the block's
+// class, and leaves the combinatorial index out of the kernel altogether.  The
+// Tetra summary (arXiv 2609.35465, section 5.1) gives the epilogue order: the
+// row scale first, then the unquantized tail.
 //
 // gfx950 design.  One wave64 owns one row at a time (rows are grid-strided
 // over all waves).  Lane l takes blocks l, l + 64, ... of the row, so every
@@ -44,6 +44,7 @@ constexpr int kMaxWgThreads = 1024;
 // blocks per lane per work item: the code words of the current and the next
 // item must stay in registers (no spills) next to B accumulator pairs
 constexpr int max_bpl(int B) { return B <= 2 ? 4 : 2; }
+constexpr int kMaxDevices = 64;
 
 // Workgroup size for `rows` rows: 1024 threads (x staged once per 16 waves)
 // when there are rows for 16 waves on every CU, smaller otherwise so the rows
@@ -179,6 +180,17 @@ constexpr int kMaxFused = 4;
 // epilogue
 constexpr int kSingle = 0, kFused = 1, kNoWeights = 2, kGain = 3, kLp2 = 4, kRot = 5,
               kDirect = 6, kOneHot = 7, kLp2x = 8;
+// Rows of two or three 64-block chunks (64 < nb <= 192, K <= 4608) with rows
+// to fill the chip: one block per lane and a ring of three register sets, so
+// that a row is in flight whole (measured on MI355X: 4096 x 4096 batch 1 5.08
+// -> 4.72 us, 12288 x 4096 8.79 -> 8.37 us; more items in flight on longer
+// rows was slower at every depth tried).  Single-matrix launches only: the
+// fused multi-matrix launch (per-item matrix selection) and the rotating one
+// (its prologue) measured slower with it.
+inline bool short_rows(int mode, int nb, int rows) {
+  return mode != kFused && mode != kRot && nb > 64 && nb <= 3 * 64 && rows >= 2048;
+}
+
 constexpr bool is_lp2(int M) { return M == kLp2 || M == kLp2x; }
 // 32-bit code words per block
 constexpr int words_of(int M) { return M == kDirect || M == kOneHot ? 4 : 3; }
@@ -241,12 +253,15 @@ __device__ __forceinline__ int start_of(const MatSet& ms, int m) {
 // are wave-uniform (scalar registers): each item's addresses are scalar buffer
 // resources plus a fixed per-lane offset, so no vector instruction is spent on
 // addressing.
+// The 16-bit fields stay 16-bit: widened where they are used, not where they
+// are loaded, so that no wait for them is placed ahead of the decode that
+// needs them (a widening at the load is a use of the loaded register).
 template <int BPL, int M>
 struct ItemRegs {
   uint32_t w[BPL][words_of(M)];
-  uint32_t c[BPL];
-  uint32_t tail;   // this lane's tail value (0 for lanes >= tau)
-  uint32_t scale;  // the row's fp16 scale
+  uint16_t c[BPL];
+  uint16_t tail;   // this lane's tail value (0 for lanes >= tau)
+  uint16_t scale;  // the row's fp16 scale
   uint32_t e0, e1;  // kLp2x: the row's side-channel entries [e0, e1) (uniform)
 };
 
@@ -271,8 +286,8 @@ __device__ __forceinline__ uint32_t lp2_pair(uint32_t word, int v, uint32_t lut_
 // memory, so the instructions, waits and registers are those of the real
 // kernel and no weight byte is read (0 decodes as class 0, scale 0: y = +0).
 template <int M>
-__device__ __forceinline__ uint32_t weight_bytes(uint32_t n) {
-  return M == kNoWeights ? 0u : n;
+__device__ __forceinline__ uint32_t weight_bytes(uint32_t n, bool valid) {
+  return M == kNoWeights || !valid ? 0u : n;
 }
 
 // A lane's byte offsets into an item's class ids / tail values (2 bytes per
@@ -293,7 +308,7 @@ __device__ __forceinline__ int opaque(int& v) {
 
 template <int BPL, int M>
 __device__ __forceinline__ void load_meta(const MatSet& ms, int nb, int tau, int gr, int chunk,
-                                          LaneOff& lo, ItemRegs<BPL, M>& g) {
+                                          bool valid, LaneOff& lo, ItemRegs<BPL, M>& g) {
   const int lo2 = opaque(lo.meta);
   const int m = mat_of<M>(ms, gr);
   const int r = gr - start_of<M>(ms, m);
@@ -303,19 +318,19 @@ __device__ __forceinline__ void load_meta(const MatSet& ms, int nb, int tau, int
   const int k0 = chunk * (kWave * BPL);
   if (!is_lp2(M) && M != kDirect) {  // LP2 keeps the class in the record; direct has none
     const auto rc =
-        buffer_rsrc(cls + (size_t)r * nb + k0, weight_bytes<M>((uint32_t)(nb - k0) * 2));
+        buffer_rsrc(cls + (size_t)r * nb + k0, weight_bytes<M>((uint32_t)(nb - k0) * 2, valid));
 #pragma unroll
     for (int u = 0; u < BPL; ++u)
       g.c[u] = __builtin_amdgcn_raw_buffer_load_b16(rc, lo2 + u * (kWave * 2), 0, kStream);
   }
-  const auto rt = buffer_rsrc(tail + (size_t)r * tau, weight_bytes<M>((uint32_t)tau * 2));
+  const auto rt = buffer_rsrc(tail + (size_t)r * tau, weight_bytes<M>((uint32_t)tau * 2, valid));
   g.tail = __builtin_amdgcn_raw_buffer_load_b16(rt, lo2, 0, 0);
   // the row scale, read by every lane (one transaction); a vector load, so
   // that waiting for it never holds up the LDS reads
-  const auto rs = buffer_rsrc(scale + r, weight_bytes<M>(2));
+  const auto rs = buffer_rsrc(scale + r, weight_bytes<M>(2, valid));
   g.scale = __builtin_amdgcn_raw_buffer_load_b16(rs, 0, 0, 0);
   if constexpr (M == kLp2x) {
-    const auto re = buffer_rsrc(ms.exc_off + r, 8);
+    const auto re = buffer_rsrc(ms.exc_off + r, valid ? 8u : 0u);
     g.e0 = __builtin_amdgcn_raw_buffer_load_b32(re, 0, 0, 0);
     g.e1 = __builtin_amdgcn_raw_buffer_load_b32(re, 4, 0, 0);
   }
@@ -327,7 +342,7 @@ typedef const __attribute__((address_space(3))) u32x4_t lds_u32x4;
 
 template <int BPL, int M>
 __device__ __forceinline__ void load_codes(const MatSet& ms, int nb, int gr, int chunk,
-                                           LaneOff& loff, ItemRegs<BPL, M>& g) {
+                                           bool valid, LaneOff& loff, ItemRegs<BPL, M>& g) {
   const int lo = opaque(loff.codes);
   const int m = mat_of<M>(ms, gr);
   const int r = gr - start_of<M>(ms, m);
@@ -335,7 +350,8 @@ __device__ __forceinline__ void load_codes(const MatSet& ms, int nb, int gr, int
   const int k0 = chunk * (kWave * BPL);
   if constexpr (M == kDirect || M == kOneHot) {
     // one 16-byte record per block
-    const auto rw = buffer_rsrc(codes + ((size_t)r * nb + k0) * 4, (uint32_t)(nb - k0) * 16);
+    const auto rw = buffer_rsrc(codes + ((size_t)r * nb + k0) * 4,
+                                weight_bytes<M>((uint32_t)(nb - k0) * 16, valid));
 #pragma unroll
     for (int u = 0; u < BPL; ++u) {
       const auto v = __builtin_bit_cast(
@@ -348,7 +364,7 @@ __device__ __forceinline__ void load_codes(const MatSet& ms, int nb, int gr, int
     return;
   } else {
   const auto rw = buffer_rsrc(codes + ((size_t)r * nb + k0) * 3,
-                              weight_bytes<M>((uint32_t)(nb - k0) * 12));
+                              weight_bytes<M>((uint32_t)(nb - k0) * 12, valid));
 #pragma unroll
   for (int u = 0; u < BPL; ++u) {
     const int o = lo + u * (kWave * 12);
@@ -362,9 +378,9 @@ __device__ __forceinline__ void load_codes(const MatSet& ms, int nb, int gr, int
 // Both groups, metadata first, so a table lookup never waits for code words.
 template <int BPL, int M>
 __device__ __forceinline__ void load_item(const MatSet& ms, int nb, int tau, int gr, int chunk,
-                                          LaneOff& lo, ItemRegs<BPL, M>& g) {
-  load_meta<BPL, M>(ms, nb, tau, gr, chunk, lo, g);
-  load_codes<BPL, M>(ms, nb, gr, chunk, lo, g);
+                                          bool valid, LaneOff& lo, ItemRegs<BPL, M>& g) {
+  load_meta<BPL, M>(ms, nb, tau, gr, chunk, valid, lo, g);
+  load_codes<BPL, M>(ms, nb, gr, chunk, valid, lo, g);
 }
 
 // LDS layout (dynamic): lut uint2[302] | x fp16 [B][kpad], kpad >= 24 * npad and
@@ -558,9 +574,9 @@ __device__ __forceinline__ uint2 stage_lut(int c, uint64_t entry) {
 // the rotating mode, whose prologue holds 16-value butterfly sets, LP2
 // above batch 1, whose class extraction needs the registers, and the one-hot
 // mode, which keeps a block's four masks and its steps live across 12 pairs.)
-constexpr int leech_min_waves(int B, int BPL, int M) {
+constexpr int leech_min_waves(int B, int BPL, int M, int D) {
   return M != kGain && M != kRot && M != kOneHot && M != kLp2x && !(M == kLp2 && B > 1) &&
-                 B + BPL <= 4
+                 B + (D * BPL + 1) / 2 <= 4
              ? 8
              : 1;
 }
@@ -822,9 +838,9 @@ __device__ __forceinline__ void rotate_x_lds(uint16_t* xh, float* fb, const floa
   }
 }
 
-template <int B, int BPL, int M>
+template <int B, int BPL, int M, int D>
 __global__ void __launch_bounds__(kMaxWgThreads)
-__attribute__((amdgpu_waves_per_eu(leech_min_waves(B, BPL, M))))
+__attribute__((amdgpu_waves_per_eu(leech_min_waves(B, BPL, M, D))))
 leech_gemv_kernel(MatSet ms, int rows, int nb, int tau, int cols, int nchunks, int kpad,
                   const uint16_t* __restrict__ x) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
@@ -847,9 +863,16 @@ leech_gemv_kernel(MatSet ms, int rows, int nb, int tau, int cols, int nchunks, i
   //    that write LDS directly, 1 KiB per wave instruction, columns past
   //    cols reading as 0 (kpad is a multiple of 512 columns, so a 1 KiB unit
   //    never straddles two batch rows).  Otherwise element by element.
+  //    Up to 32 KiB the copies are issued by the first four waves only:
+  //    waves start in order, so their copies enter the CU's memory queue
+  //    ahead of most weight loads and the barrier below is not held up by a
+  //    late wave's copies queued behind other waves' weight loads (measured:
+  //    7.70 -> 7.45 us at 4096 x 12288, batch 1).  Larger copies go to every
+  //    wave (issuing 24+ copies per wave costs more than it saves).
   if (vec) {
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-    for (int q = wv; q * kWave < nq; q += wpb) {
+    const int nx = nq > 32 * kWave || wpb < 4 ? wpb : 4;
+    for (int q = wv < nx ? wv : nq; q * kWave < nq; q += nx) {
       const int u0 = q * kWave;  // first 16-byte unit of this KiB
       const int bb = B == 1 ? 0 : u0 / per;
       const int c0 = 8 * (u0 - bb * per);
@@ -897,17 +920,25 @@ leech_gemv_kernel(MatSet ms, int rows, int nb, int tau, int cols, int nchunks, i
   const uint64_t* table = ms.v[0].table;  // the same universal table in every blob
   const uint64_t te = M == kDirect ? 0 : table[min(tid, LVQ_NUM_CLASSES - 1)];
   asm volatile("" ::: "memory");
-  // 2. the first two items (a wave with fewer items loads rows it never
-  //    uses, so that the load sequence has no branches and every later wait
-  //    counts exactly)
-  ItemRegs<BPL, M> ia, ib;
+  // 2. the first D items, one in each register set of the ring.  Item j of
+  //    this wave is row wave + (j / nchunks) nwaves, chunk j % nchunks.  A set
+  //    whose item lies past the wave's last is loaded from an empty range (no
+  //    memory request, every value 0), so the load sequence has no branch and
+  //    every later wait counts exactly.
+  ItemRegs<BPL, M> ring[D];
+  int rr[D], rc[D];
   LaneOff lo = {lane * 2, lane * 4 * words_of(M)};
   lds_u32* const xlane = (lds_u32*)xs + lane * 12;
-  int ra = wave < rows ? wave : 0, ca = 0;
-  int rb = ca + 1 == nchunks ? ra + nwaves : ra, cb = ca + 1 == nchunks ? 0 : ca + 1;
-  if (items < 2) { rb = ra; cb = ca; }
-  load_item<BPL, M>(ms, nb, tau, ra, ca, lo, ia);
-  load_item<BPL, M>(ms, nb, tau, rb, cb, lo, ib);
+  {
+    int r = wave, c = 0;
+#pragma unroll
+    for (int s = 0; s < D; ++s) {
+      rr[s] = r;
+      rc[s] = c;
+      load_item<BPL, M>(ms, nb, tau, r, c, s < items, lo, ring[s]);
+      if (++c == nchunks) { c = 0; r += nwaves; }
+    }
+  }
   asm volatile("" ::: "memory");
   // 3. the class table into LDS; the barrier also waits for x
   for (int c = tid; M != kDirect && c < LVQ_NUM_CLASSES; c += nthr) {
@@ -925,34 +956,28 @@ leech_gemv_kernel(MatSet ms, int rows, int nb, int tau, int cols, int nchunks, i
 #pragma unroll
   for (int bb = 0; bb < B; ++bb) acc[bb][0] = acc[bb][1] = acc[bb][2] = 0.f;
   if (items == 0) return;
-  // steady state, two items per trip with the register sets ia and ib: decode
-  // one while the other and the next one are in flight
+  // steady state: set s holds item j + s; decode it, then load item j + s + D
+  // into the same registers, so D - 1 items stay in flight behind each decode
   auto advance = [&](int& r, int& c) {
-    // the item two places further: (r, c) -> next -> next
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      if (c + 1 == nchunks) { r += nwaves; c = 0; } else { ++c; }
-    }
+    c += D;
+    while (c >= nchunks) { c -= nchunks; r += nwaves; }
   };
   int j = 0;
-  for (; j + 3 < items; j += 2) {
-    decode_item<B, BPL, M>(ms, nb, tau, nchunks, kpad, ra, ca, lane, ia, lut, xs, xlane, acc);
-    advance(ra, ca);
-    load_item<BPL, M>(ms, nb, tau, ra, ca, lo, ia);
-    decode_item<B, BPL, M>(ms, nb, tau, nchunks, kpad, rb, cb, lane, ib, lut, xs, xlane, acc);
-    advance(rb, cb);
-    load_item<BPL, M>(ms, nb, tau, rb, cb, lo, ib);
+  for (; j + D < items; j += D) {
+#pragma unroll
+    for (int s = 0; s < D; ++s) {
+      decode_item<B, BPL, M>(ms, nb, tau, nchunks, kpad, rr[s], rc[s], lane, ring[s], lut, xs,
+                             xlane, acc);
+      advance(rr[s], rc[s]);
+      load_item<BPL, M>(ms, nb, tau, rr[s], rc[s], j + s + D < items, lo, ring[s]);
+    }
   }
-  // the last one to three items
-  decode_item<B, BPL, M>(ms, nb, tau, nchunks, kpad, ra, ca, lane, ia, lut, xs, xlane, acc);
-  if (j + 2 < items) {
-    advance(ra, ca);
-    load_item<BPL, M>(ms, nb, tau, ra, ca, lo, ia);
-  }
-  if (j + 1 < items)
-    decode_item<B, BPL, M>(ms, nb, tau, nchunks, kpad, rb, cb, lane, ib, lut, xs, xlane, acc);
-  if (j + 2 < items)
-    decode_item<B, BPL, M>(ms, nb, tau, nchunks, kpad, ra, ca, lane, ia, lut, xs, xlane, acc);
+  // the last one to D items, in sets 0 .. items - j - 1
+#pragma unroll
+  for (int s = 0; s < D; ++s)
+    if (j + s < items)
+      decode_item<B, BPL, M>(ms, nb, tau, nchunks, kpad, rr[s], rc[s], lane, ring[s], lut, xs,
+                             xlane, acc);
 }
 
 // Rows shorter than one block: y = sum of the unquantized tail only.
@@ -1001,31 +1026,33 @@ __global__ void zero_kernel(float* y, size_t n) {
   if (i < n) y[i] = 0.f;
 }
 
+// Device attributes, cached per device id (ints written whole, with the same
+// value by any thread that races on them).
 int device_cus() {
-  static int cached[64] = {0};
+  static int cached[kMaxDevices];
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (!cached[dev]) {
-    int n = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
+  int n = __atomic_load_n(&cached[dev], __ATOMIC_RELAXED);
+  if (!n) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
       n = 256;
-    cached[dev] = n;
+    __atomic_store_n(&cached[dev], n, __ATOMIC_RELAXED);
   }
-  return cached[dev];
+  return n;
 }
 
 size_t device_lds_bytes() {
-  static size_t cached[64] = {0};
+  static int cached[kMaxDevices];
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 65536;
-  if (!cached[dev]) {
-    int n = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 65536;
+  int n = __atomic_load_n(&cached[dev], __ATOMIC_RELAXED);
+  if (!n) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess ||
         n <= 0)
       n = 65536;
-    cached[dev] = (size_t)n;
+    __atomic_store_n(&cached[dev], n, __ATOMIC_RELAXED);
   }
-  return cached[dev];
+  return (size_t)n;
 }
 
 int zero_output(float* y, size_t n, hipStream_t st) {
@@ -1035,7 +1062,28 @@ int zero_output(float* y, size_t n, hipStream_t st) {
   return launch_status();
 }
 
-template <int B, int BPL, int M>
+// Workgroups per CU that fit at once for a kernel, by the occupancy query,
+// cached per device and per (workgroup size, LDS above 64 KiB).  The cache
+// entries are ints written whole with the same value by any thread that
+// races on them.
+template <typename K>
+int wgs_per_cu(K kernel, int threads, size_t lds) {
+  static int cached[kMaxDevices][3][2];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) dev = 0;
+  const int ti = threads == 1024 ? 0 : threads == 512 ? 1 : 2, li = lds > 64 * 1024;
+  int n = __atomic_load_n(&cached[dev][ti][li], __ATOMIC_RELAXED);
+  if (!n) {
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, threads, lds) != hipSuccess ||
+        n < 1)
+      n = 1;
+    n = n > 2 ? 2 : n;
+    __atomic_store_n(&cached[dev][ti][li], n, __ATOMIC_RELAXED);
+  }
+  return n;
+}
+
+template <int B, int BPL, int M, int D>
 int launch_leech_mode(const MatSet& ms, int rows, int cols, const uint16_t* x, hipStream_t st) {
   const int nb = cols / 24, tau = cols % 24;
   const int nchunks = (nb + kWave * BPL - 1) / (kWave * BPL);
@@ -1054,22 +1102,22 @@ int launch_leech_mode(const MatSet& ms, int rows, int cols, const uint16_t* x, h
   const int wpb = threads / kWave;
   // as many workgroups as fit on the chip at once (one or two per CU, by
   // registers and LDS), rows grid-strided over their waves
-  static int occupancy[3][2] = {{0, 0}, {0, 0}, {0, 0}};
-  const int ti = threads == 1024 ? 0 : threads == 512 ? 1 : 2, li = lds > 64 * 1024;
-  if (!occupancy[ti][li]) {
-    int n = 1;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, leech_gemv_kernel<B, BPL, M>, threads,
-                                                     lds) != hipSuccess || n < 1)
-      n = 1;
-    occupancy[ti][li] = n > 2 ? 2 : n;
-  }
+  const int occ = wgs_per_cu(leech_gemv_kernel<B, BPL, M, D>, threads, lds);
   long long wgs = ((long long)rows + wpb - 1) / wpb;
-  if (wgs > (long long)occupancy[ti][li] * cus) wgs = (long long)occupancy[ti][li] * cus;
+  if (wgs > (long long)occ * cus) wgs = (long long)occ * cus;
   if (wgs < 1) wgs = 1;
   clear_hip_error();
-  hipLaunchKernelGGL((leech_gemv_kernel<B, BPL, M>), dim3((unsigned)wgs), dim3(threads), lds, st,
-                     ms, rows, nb, tau, cols, nchunks, (int)kpad, x);
+  hipLaunchKernelGGL((leech_gemv_kernel<B, BPL, M, D>), dim3((unsigned)wgs), dim3(threads), lds,
+                     st, ms, rows, nb, tau, cols, nchunks, (int)kpad, x);
   return launch_status();
+}
+
+template <int B, int BPL, int M>
+int launch_leech_ring(const MatSet& ms, int rows, int cols, const uint16_t* x, hipStream_t st) {
+  if constexpr (BPL == 1 && M != kFused && M != kRot) {
+    if (short_rows(M, cols / 24, rows)) return launch_leech_mode<B, BPL, M, 3>(ms, rows, cols, x, st);
+  }
+  return launch_leech_mode<B, BPL, M, 2>(ms, rows, cols, x, st);
 }
 
 // the shape-gain mode's extra partial sums, and the rotating mode's prologue,
@@ -1079,19 +1127,19 @@ constexpr bool gain_bpl_ok(int B, int BPL) { return !(B >= 2 && BPL >= 4); }
 template <int B, int BPL>
 int launch_leech_bpl(const MatSet& ms, int mode, int rows, int cols, const uint16_t* x,
                      hipStream_t st) {
-  if (mode == kFused) return launch_leech_mode<B, BPL, kFused>(ms, rows, cols, x, st);
-  if (mode == kNoWeights) return launch_leech_mode<B, BPL, kNoWeights>(ms, rows, cols, x, st);
+  if (mode == kFused) return launch_leech_ring<B, BPL, kFused>(ms, rows, cols, x, st);
+  if (mode == kNoWeights) return launch_leech_ring<B, BPL, kNoWeights>(ms, rows, cols, x, st);
   if constexpr (gain_bpl_ok(B, BPL)) {
-    if (mode == kGain) return launch_leech_mode<B, BPL, kGain>(ms, rows, cols, x, st);
+    if (mode == kGain) return launch_leech_ring<B, BPL, kGain>(ms, rows, cols, x, st);
   }
-  if (mode == kLp2) return launch_leech_mode<B, BPL, kLp2>(ms, rows, cols, x, st);
-  if (mode == kLp2x) return launch_leech_mode<B, BPL, kLp2x>(ms, rows, cols, x, st);
-  if (mode == kDirect) return launch_leech_mode<B, BPL, kDirect>(ms, rows, cols, x, st);
-  if (mode == kOneHot) return launch_leech_mode<B, BPL, kOneHot>(ms, rows, cols, x, st);
+  if (mode == kLp2) return launch_leech_ring<B, BPL, kLp2>(ms, rows, cols, x, st);
+  if (mode == kLp2x) return launch_leech_ring<B, BPL, kLp2x>(ms, rows, cols, x, st);
+  if (mode == kDirect) return launch_leech_ring<B, BPL, kDirect>(ms, rows, cols, x, st);
+  if (mode == kOneHot) return launch_leech_ring<B, BPL, kOneHot>(ms, rows, cols, x, st);
   if constexpr (gain_bpl_ok(B, BPL)) {
-    if (mode == kRot) return launch_leech_mode<B, BPL, kRot>(ms, rows, cols, x, st);
+    if (mode == kRot) return launch_leech_ring<B, BPL, kRot>(ms, rows, cols, x, st);
   }
-  return launch_leech_mode<B, BPL, kSingle>(ms, rows, cols, x, st);
+  return launch_leech_ring<B, BPL, kSingle>(ms, rows, cols, x, st);
 }
 
 // rows = total rows of the set; rows shorter than one block go to the
@@ -1117,8 +1165,12 @@ int launch_leech(const MatSet& ms, int n, int mode, int rows, int cols, const ui
     }
     return LVQ_OK;
   }
-  const int bpl =
-      choose_bpl(nb, (mode == kGain || mode == kRot) && B >= 2 ? 3 : max_bpl(B), rows, device_cus());
+  // short rows (short_rows): one block per lane, the whole row in flight;
+  // otherwise the blocks-per-lane rule
+  const int bpl = short_rows(mode, nb, rows)
+                      ? 1
+                      : choose_bpl(nb, (mode == kGain || mode == kRot) && B >= 2 ? 3 : max_bpl(B),
+                                   rows, device_cus());
   if constexpr (max_bpl(B) >= 4) {
     if (bpl == 4) {
       const int e = launch_leech_bpl<B, 4>(ms, mode, rows, cols, x, st);
