@@ -41,6 +41,8 @@ import re
 import sys
 import time
 
+import numpy as np
+
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
@@ -63,6 +65,10 @@ def parse():
     p.add_argument("--stack-layers", type=int, default=QWEN_LAYERS)
     p.add_argument("--profile", choices=["leech", "noweights", "direct", "fp16", "bpdq", "trellis", "copy"], default=None)
     p.add_argument("--profile-batch", type=int, default=1, choices=[1, 2, 3, 4])
+    p.add_argument("--ceiling", action="store_true",
+                   help="sweep the launch shape of a plain read of the headline's bytes "
+                        "(the streaming ceiling) and time a device-to-device copy of them")
+    p.add_argument("--ceiling-bytes", type=int, default=None)
     return p.parse_args()
 
 
@@ -88,6 +94,17 @@ def _stack_worker(job):
     d = synth.qwen3_8b_matrix(layer, matrix)
     blob = lvq.expand(d["coords"], d["scale"], d["tail"], d["rows"], d["cols"])
     return layer, matrix, d["rows"], d["cols"], blob
+
+
+def _stack_check(job):
+    """The oracle leg's check of one stack GEMV, run in a worker process:
+    (layer, matrix, x fp16 bits, y) -> (layer, matrix, parity ratio)."""
+    import synth
+    from oracle import gemv as og
+    layer, matrix, x_bits, y = job
+    d = synth.qwen3_8b_matrix(layer, matrix)
+    y64, bound = og.gemv(og.leech_weights(d["coords"], d["scale"], d["tail"], d["cols"]), x_bits)
+    return layer, matrix, og.check(y, y64, bound)
 
 
 def start_stack_pool(layers):
@@ -241,13 +258,116 @@ def fp16_bytes(rows, cols):
     return 2 * rows * cols
 
 
+# ---------------------------------------------------------------- oracle leg
+
+class ParityGateError(RuntimeError):
+    pass
+
+
+class OracleLeg:
+    """The cpu_baseline leg: the f64 oracle (test infrastructure) on the host
+    cores.  Every arm's GPU output at the shape and launch it is timed in is
+    checked here before that arm is timed: |y - y_f64| <= 1e-4 * sum_c |w x|
+    per output (activation rotations: one fp16 ulp plus 1e-5 of the term
+    magnitudes), decoded lattice points and unfolded words bit-exact.  The
+    first failure stops the run (non-zero exit, no result line).  The same leg
+    times the oracle on the headline workload (cpu_baseline)."""
+
+    def __init__(self, enabled):
+        self.enabled = enabled
+        self.ratios = {}
+
+    def _done(self, name, r, bar=1.0):
+        self.ratios[name] = round(float(r), 5)
+        if not r <= bar:
+            raise ParityGateError("%s: parity ratio %.4g exceeds %.3g" % (name, r, bar))
+        return r
+
+    def weights(self, name, w_fn, x, y):
+        """w_fn() -> f64 W [rows][cols]; x fp16 bits [batch][cols]; y GPU fp32."""
+        if not self.enabled:
+            return None
+        from oracle import gemv as og
+        y64, bound = og.gemv(w_fn(), x)
+        return self._done(name, og.check(y, y64, bound))
+
+    def leech(self, name, d, x, y):
+        if not self.enabled:
+            return None
+        from oracle import gemv as og
+        return self.weights(name, lambda: og.leech_weights(d["coords"], d["scale"], d["tail"],
+                                                          d["cols"]), x, y)
+
+    def fp16(self, name, wb, rows, cols, x, y):
+        if not self.enabled:
+            return None
+        from oracle import gemv as og
+        return self.weights(name, lambda: og.fp16_weights(wb, rows, cols), x, y)
+
+    def bpdq(self, name, d, x, y):
+        if not self.enabled:
+            return None
+        from oracle import gemv as og
+        return self.weights(name, lambda: og.bpdq_weights(d["codes"], d["coeffs"], d["rows"],
+                                                          d["cols"]), x, y)
+
+    def trellis(self, name, d, x, y):
+        if not self.enabled:
+            return None
+        from oracle import gemv as og
+        return self.weights(name, lambda: og.trellis_weights(d["bits"], d["table"], d["scale"],
+                                                             d["rows"], d["cols"]), x, y)
+
+    def bitexact(self, name, ok):
+        self.ratios[name] = bool(ok)
+        if not ok:
+            raise ParityGateError("%s: not bit-exact" % name)
+        return ok
+
+    def rotation(self, name, x, n, m, words, q, y_bits):
+        if not self.enabled:
+            return None
+        from oracle import rotate as orot
+        y64, bound = orot.rotate(x, n, m, words, q)
+        return self._done(name, orot.rotate_check(y_bits, y64, bound))
+
+    def unfold(self, name, words, coords, gains):
+        if not self.enabled:
+            return None
+        from oracle import index as oi
+        ok = True
+        for i, w in enumerate(words):
+            idx, g = oi.split_word(int(w))
+            ok &= bool(np.array_equal(coords[i], oi.unrank(idx))) and int(gains[i]) == g
+        return self.bitexact(name, ok)
+
+    def gain(self, name, d, gbits, gains, x, y):
+        if not self.enabled:
+            return None
+        from oracle import index as oi
+        return self.weights(name, lambda: oi.shape_gain_weights(
+            d["coords"], gbits, d["scale"], gains, d["tail"], d["cols"]), x, y)
+
+    def worst(self):
+        r = [v for v in self.ratios.values() if not isinstance(v, bool)]
+        return max(r) if r else None
+
+
 # ---------------------------------------------------------------- records
 
 class Bench:
-    def __init__(self, torch, lvq, args, props):
+    def __init__(self, torch, lvq, args, props, leg):
         self.torch, self.lvq, self.args, self.props = torch, lvq, args, props
+        self.leg = leg
         self.sink = torch.zeros(lvq.STREAM_SINK_WORDS, dtype=torch.int32, device="cuda")
         self.ceiling = {}
+
+    def first(self, fn, yd):
+        """One launch of the timed call (copy 0), its output on the host: what
+        the oracle leg checks before the call is timed."""
+        fn(0)
+        self.torch.cuda.synchronize()
+        return yd.cpu().numpy()
 
     def time(self, fn, steps=None):
         a = self.args
@@ -294,7 +414,6 @@ class Bench:
 
     # one Leech matrix at one shape and batch
     def leech(self, cfg, rows, cols, batch, d=None, keep=False):
-        import numpy as np
         import synth
         torch, lvq = self.torch, self.lvq
         if d is None:
@@ -306,24 +425,31 @@ class Bench:
         bufs = dev_copies(torch, blob, n)
         xd = to_dev(torch, x)
         yd = torch.empty((batch, rows), dtype=torch.float32, device="cuda")
-        tm = self.time(lambda i: lvq.gemv(bufs[i % n], rows, cols, xd, yd, batch))
-        # the no-weights control: the same launch reading no weight bytes
-        y0 = torch.empty_like(yd)
-        t0 = self.time(lambda i: lvq.gemv_noweights(bufs[i % n], rows, cols, xd, y0, batch))
-        rec = self.record("leech", cfg, rows, cols, batch, nbytes, n, tm,
-                          blob_bytes=int(blob.size), us_noweights=round(t0.median, 3),
-                          pct_time_noweights=round(100 * t0.median / tm.median, 1))
-        out = (rec, d, x, yd.cpu().numpy()) if keep else rec
+        shape = "%dx%d b%d" % (rows, cols, batch)
+        gate = {}
         if keep:
-            self.graph_us = self.graph(lambda i: lvq.gemv(bufs[i % n], rows, cols, xd, yd, batch))
             # the bit-exact gate: the timed blob decodes to the input points on
             # the GPU, and they re-expand to the same blob
             dec = torch.empty((rows, cols // 24, 24), dtype=torch.int8, device="cuda")
             lvq.decode(bufs[0], rows, cols, dec)
             got = dec.cpu().numpy()
-            rec["bitexact"] = bool(np.array_equal(got, d["coords"]) and np.array_equal(
+            gate["bitexact"] = self.leg.bitexact("lvq_decode " + shape, np.array_equal(
+                got, d["coords"]) and np.array_equal(
                 lvq.expand(got, d["scale"], d["tail"], rows, cols), blob))
             del dec
+        fn = lambda i: lvq.gemv(bufs[i % n], rows, cols, xd, yd, batch)  # noqa: E731
+        gate["parity_max_ratio"] = self.leg.leech("lvq_gemv cfg%d %s" % (cfg, shape), d, x,
+                                                  self.first(fn, yd))
+        tm = self.time(fn)
+        # the no-weights control: the same launch reading no weight bytes
+        y0 = torch.empty_like(yd)
+        t0 = self.time(lambda i: lvq.gemv_noweights(bufs[i % n], rows, cols, xd, y0, batch))
+        rec = self.record("leech", cfg, rows, cols, batch, nbytes, n, tm,
+                          blob_bytes=int(blob.size), us_noweights=round(t0.median, 3),
+                          pct_time_noweights=round(100 * t0.median / tm.median, 1), **gate)
+        out = (rec, d, x) if keep else rec
+        if keep:
+            self.graph_us = self.graph(fn)
         del bufs
         torch.cuda.empty_cache()
         return out
@@ -369,10 +495,13 @@ class Bench:
         bufs = dev_copies(torch, wb, n)
         xd = to_dev(torch, x)
         yd = torch.empty((batch, rows), dtype=torch.float32, device="cuda")
-        tm = self.time(lambda i: lvq.fp16_gemv(bufs[i % n], rows, cols, xd, yd, batch))
+        fn = lambda i: lvq.fp16_gemv(bufs[i % n], rows, cols, xd, yd, batch)  # noqa: E731
+        r = self.leg.fp16("fp16_gemv %dx%d b%d" % (rows, cols, batch), wb, rows, cols, x,
+                          self.first(fn, yd))
+        tm = self.time(fn)
         del bufs
         torch.cuda.empty_cache()
-        return self.record("fp16", cfg, rows, cols, batch, nbytes, n, tm)
+        return self.record("fp16", cfg, rows, cols, batch, nbytes, n, tm, parity_max_ratio=r)
 
     def bpdq(self, rows, cols, batch):
         import synth
@@ -385,11 +514,13 @@ class Bench:
         coeffs = dev_copies(torch, d["coeffs"], n)
         xd = to_dev(torch, x)
         yd = torch.empty((batch, rows), dtype=torch.float32, device="cuda")
-        tm = self.time(lambda i: lvq.bpdq_gemv(codes[i % n], coeffs[i % n], rows, cols, xd, yd,
-                                              batch))
+        fn = lambda i: lvq.bpdq_gemv(codes[i % n], coeffs[i % n], rows, cols, xd, yd,  # noqa
+                                     batch)
+        r = self.leg.bpdq("bpdq_gemv %dx%d b%d" % (rows, cols, batch), d, x, self.first(fn, yd))
+        tm = self.time(fn)
         del codes, coeffs
         torch.cuda.empty_cache()
-        return self.record("bpdq", 2, rows, cols, batch, nbytes, n, tm)
+        return self.record("bpdq", 2, rows, cols, batch, nbytes, n, tm, parity_max_ratio=r)
 
     def trellis(self, rows, cols, batch):
         import synth
@@ -403,11 +534,14 @@ class Bench:
         scale = to_dev(torch, d["scale"])
         xd = to_dev(torch, x)
         yd = torch.empty((batch, rows), dtype=torch.float32, device="cuda")
-        tm = self.time(lambda i: lvq.trellis_gemv(bits[i % n], table, scale, rows, cols, xd, yd,
-                                                 batch))
+        fn = lambda i: lvq.trellis_gemv(bits[i % n], table, scale, rows, cols, xd, yd,  # noqa
+                                        batch)
+        r = self.leg.trellis("trellis_gemv %dx%d b%d" % (rows, cols, batch), d, x,
+                             self.first(fn, yd))
+        tm = self.time(fn)
         del bits
         torch.cuda.empty_cache()
-        return self.record("trellis", 4, rows, cols, batch, nbytes, n, tm)
+        return self.record("trellis", 4, rows, cols, batch, nbytes, n, tm, parity_max_ratio=r)
 
     def unfold(self, nblocks):
         """Load-time unfolding of random 48-bit words (one per 24-weight block)."""
@@ -422,12 +556,16 @@ class Bench:
         gd = torch.empty(nblocks, dtype=torch.uint8, device="cuda")
         lvq.unfold(wd, nblocks, cd, gd)  # uploads the tables once
         torch.cuda.synchronize()
+        pick = np.random.default_rng(1).choice(nblocks, 256, replace=False)
+        ok = self.leg.unfold("lvq_unfold %d words (256 sampled)" % nblocks, words[pick],
+                             cd.cpu().numpy()[pick], gd.cpu().numpy()[pick])
         tm = Timed(torch, lambda i: lvq.unfold(wd, nblocks, cd, gd), 20, 3, self.args.trials)
         us = tm.median
         rec = {"arm": "unfold", "blocks": nblocks, "weights": 24 * nblocks,
                "us_median": round(us, 1), "us_min": round(tm.us[0], 1),
                "gblocks_per_s": round(nblocks / (us * 1e-6) / 1e9, 3),
-               "bytes_in": 8 * nblocks, "bytes_out": 25 * nblocks, "trials": self.args.trials}
+               "bytes_in": 8 * nblocks, "bytes_out": 25 * nblocks, "trials": self.args.trials,
+               "bitexact_sample": ok}
         log("unfold   %d blocks: %.1f us (%.3f G blocks/s)" % (nblocks, us, rec["gblocks_per_s"]))
         return rec
 
@@ -443,11 +581,14 @@ class Bench:
         bufs = dev_copies(torch, blob, n)
         xd = to_dev(torch, x)
         yd = torch.empty((batch, rows), dtype=torch.float32, device="cuda")
-        tm = self.time(lambda i: lvq.gemv_lp2(bufs[i % n], rows, cols, xd, yd, batch))
+        fn = lambda i: lvq.gemv_lp2(bufs[i % n], rows, cols, xd, yd, batch)  # noqa: E731
+        r = self.leg.leech("lvq_gemv_lp2 cfg%d %dx%d b%d" % (cfg, rows, cols, batch), d, x,
+                           self.first(fn, yd))
+        tm = self.time(fn)
         del bufs
         torch.cuda.empty_cache()
         return self.record("leech_lp2", cfg, rows, cols, batch, lp2_bytes(rows, cols), n, tm,
-                           blob_bytes=int(blob.size))
+                           blob_bytes=int(blob.size), parity_max_ratio=r)
 
     def leech_direct(self, cfg, rows, cols, batch, d=None):
         """The table-free direct layout (|x| = 2e + parity) at one shape."""
@@ -470,14 +611,18 @@ class Bench:
         bufs = dev_copies(torch, blob, n)
         xd = to_dev(torch, x)
         yd = torch.empty((batch, rows), dtype=torch.float32, device="cuda")
-        tm = self.time(lambda i: gemv(bufs[i % n], rows, cols, xd, yd, batch))
+        fn = lambda i: gemv(bufs[i % n], rows, cols, xd, yd, batch)  # noqa: E731
+        r = self.leg.leech("%s cfg%d %dx%d b%d" % (arm, cfg, rows, cols, batch), d, x,
+                           self.first(fn, yd))
+        tm = self.time(fn)
         del bufs
         torch.cuda.empty_cache()
         return self.record(arm, cfg, rows, cols, batch, nbytes(rows, cols), n, tm,
-                           blob_bytes=int(blob.size))
+                           blob_bytes=int(blob.size), parity_max_ratio=r)
 
     def leech_lp2x(self, cfg, rows, cols, batch, d=None):
-        """LP2 with the exception side channel (two launches) at one shape."""
+        """LP2 with the exception side channel, decoded in each row's epilogue of
+        the same launch, at one shape."""
         import synth
         torch, lvq = self.torch, self.lvq
         if d is None:
@@ -488,12 +633,16 @@ class Bench:
         bufs = dev_copies(torch, blob, n)
         xd = to_dev(torch, x)
         yd = torch.empty((batch, rows), dtype=torch.float32, device="cuda")
-        tm = self.time(lambda i: lvq.gemv_lp2x(bufs[i % n], rows, cols, n_exc, xd, yd, batch))
+        fn = lambda i: lvq.gemv_lp2x(bufs[i % n], rows, cols, n_exc, xd, yd, batch)  # noqa
+        r = self.leg.leech("lvq_gemv_lp2x cfg%d %dx%d b%d" % (cfg, rows, cols, batch), d, x,
+                           self.first(fn, yd))
+        tm = self.time(fn)
         del bufs
         torch.cuda.empty_cache()
         nbytes = lp2_bytes(rows, cols) + 16 * n_exc + 4 * (rows + 1)
         return self.record("leech_lp2x", cfg, rows, cols, batch, nbytes, n, tm,
-                           side_channel_blocks=int(n_exc), blob_bytes=int(blob.size))
+                           side_channel_blocks=int(n_exc), blob_bytes=int(blob.size),
+                           parity_max_ratio=r)
 
     def leech_gain(self, rows, cols, batch):
         """The shape-gain GEMV at one shape (random gain bits, two gain levels)."""
@@ -508,11 +657,16 @@ class Bench:
         bufs = dev_copies(torch, blob, n)
         xd = to_dev(torch, x)
         yd = torch.empty((batch, rows), dtype=torch.float32, device="cuda")
-        tm = self.time(lambda i: lvq.gemv_gain(bufs[i % n], rows, cols, 0.8125, 1.1875, xd, yd,
-                                               batch))
+        gains = (0.8125, 1.1875)
+        fn = lambda i: lvq.gemv_gain(bufs[i % n], rows, cols, gains[0], gains[1], xd, yd,  # noqa
+                                     batch)
+        r = self.leg.gain("lvq_gemv_gain %dx%d b%d" % (rows, cols, batch), d, g, gains, x,
+                          self.first(fn, yd))
+        tm = self.time(fn)
         del bufs
         torch.cuda.empty_cache()
-        return self.record("leech_gain", 4, rows, cols, batch, leech_bytes(rows, cols), n, tm)
+        return self.record("leech_gain", 4, rows, cols, batch, leech_bytes(rows, cols), n, tm,
+                           parity_max_ratio=r)
 
     def rotated_gemv(self, rows, cols, m, batch):
         """Rotation fused into the GEMV against the two launches it replaces."""
@@ -531,7 +685,17 @@ class Bench:
         qd = None if q is None else torch.from_numpy(q).cuda()
         xr = torch.empty((batch, cols), dtype=torch.int16, device="cuda")
         yd = torch.empty((batch, rows), dtype=torch.float32, device="cuda")
-        tf = self.time(lambda i: lvq.gemv_rotated(bufs[i % n], rows, cols, wd, qd, m, xd, yd, batch))
+        fn = lambda i: lvq.gemv_rotated(bufs[i % n], rows, cols, wd, qd, m, xd, yd,  # noqa
+                                        batch)
+        # the gate: the rotated input against the f64 rotation, and the fused
+        # output against the f64 GEMV on that input
+        lvq.rotate(xd, cols, m, wd, qd, xr, batch)
+        xr_bits = xr.cpu().numpy().view(np.uint16)
+        shape = "%dx%d m%d b%d" % (rows, cols, m, batch)
+        r_rot = self.leg.rotation("lvq_rotate (for lvq_gemv_rotated) " + shape, x, cols, m,
+                                  words, q, xr_bits)
+        r = self.leg.leech("lvq_gemv_rotated " + shape, d, xr_bits, self.first(fn, yd))
+        tf = self.time(fn)
 
         def two(i):
             lvq.rotate(xd, cols, m, wd, qd, xr, batch)
@@ -540,7 +704,8 @@ class Bench:
         del bufs
         torch.cuda.empty_cache()
         return self.record("leech_rot", 3, rows, cols, batch, leech_bytes(rows, cols), n, tf,
-                           rot_m=m, us_rotate_then_gemv=round(t2.median, 3))
+                           rot_m=m, us_rotate_then_gemv=round(t2.median, 3),
+                           parity_max_ratio=r, rotate_parity_ratio=r_rot)
 
     def rotate(self, n, m, batch):
         """The activation rotation (H kron Q)(S x) at width n = K m."""
@@ -553,12 +718,15 @@ class Bench:
         xd, wd = to_dev(torch, x), to_dev(torch, words)
         qd = None if q is None else torch.from_numpy(q).cuda()
         yd = torch.empty((batch, n), dtype=torch.int16, device="cuda")
-        tm = self.time(lambda i: lvq.rotate(xd, n, m, wd, qd, yd, batch))
+        fn = lambda i: lvq.rotate(xd, n, m, wd, qd, yd, batch)  # noqa: E731
+        r = self.leg.rotation("lvq_rotate n%d m%d b%d" % (n, m, batch), x, n, m, words, q,
+                              self.first(fn, yd).view(np.uint16))
+        tm = self.time(fn)
         us = tm.median
         rec = {"arm": "rotate", "N": n, "m": m, "batch": batch,
                "bytes": 4 * n * batch, "us_median": round(us, 3),
                "us_min": round(tm.us[0], 3), "us_max": round(tm.us[-1], 3),
-               "reps": self.args.steps, "trials": self.args.trials}
+               "reps": self.args.steps, "trials": self.args.trials, "parity_max_ratio": r}
         log("rotate   n=%5d m=%2d b%d: %7.3f us" % (n, m, batch, us))
         return rec
 
@@ -574,7 +742,7 @@ class Bench:
             % (njobs, time.perf_counter() - t0))
         return blobs
 
-    def stack(self, blobs, layers):
+    def stack(self, blobs, layers, pool):
         import synth
         torch, lvq = self.torch, self.lvq
         total = sum(leech_bytes(r, c) for (r, c, _) in blobs.values())
@@ -620,6 +788,19 @@ class Bench:
         chain(True)
         torch.cuda.synchronize()
         order = [(li, mi) for li in range(layers) for mi in range(7)]
+        # the gate: every GEMV of the chain against the f64 oracle on its own
+        # fp16 input, in the worker pool (the oracle leg), before any timing
+        worst = None
+        if self.leg.enabled and pool is not None:
+            t0 = time.perf_counter()
+            jobs = [(li, mi, inputs[k].cpu().numpy().view(np.uint16), ys[k].cpu().numpy())
+                    for k in order for (li, mi) in [k]]
+            ratios = {(li, mi): r for li, mi, r in pool.imap_unordered(_stack_check, jobs)}
+            top = max(ratios, key=ratios.get)
+            worst = self.leg._done("lvq_gemv stack, worst of %d (layer %d, matrix %d)"
+                                   % (len(ratios), top[0], top[1]), ratios[top])
+            log("stack: all %d GEMVs within the oracle bound (worst %.3g) in %.1fs"
+                % (len(ratios), worst, time.perf_counter() - t0))
 
         def gemv_only(_):
             for li, mi in order:
@@ -677,6 +858,7 @@ class Bench:
             "gbps_fused": round(total / (tf.median * 1e-6) / 1e9, 1),
             "us_noweights": round(t0.median, 1),
             "pct_time_noweights": round(100 * t0.median / us, 1),
+            "parity_max_ratio": worst, "parity_checked_gemvs": len(order) if worst is not None else 0,
         }
         log("stack: %d GEMVs %.1f us (%.1f GB/s, %.1f%% peak); chain with renorm %.1f us"
             % (len(order), us, rec["gbps"], rec["pct_hbm_peak"], tc.median))
@@ -689,12 +871,13 @@ class Bench:
 
 # ---------------------------------------------------------------- CPU baseline
 
-def cpu_baseline(d, x, y_timed, per_shape):
+def cpu_baseline(d, x, per_shape):
     """The oracle as it stands on the host cores: the metric workload for at
     least 10 s with every core (the reported value), one core and all cores
     with the reconstruction and the matvec timed apart, and the other config
-    shapes (median of 3 with all cores)."""
-    import numpy as np
+    shapes (median of 3 with all cores).  `cores` is the thread count numpy's
+    BLAS runs the matvec with (the reconstruction is single-threaded numpy),
+    `cores_available` the cores this process may run on."""
     from threadpoolctl import threadpool_info, threadpool_limits
     from oracle import gemv as og
     import synth
@@ -710,12 +893,10 @@ def cpu_baseline(d, x, y_timed, per_shape):
         return t1 - t0, t2 - t1, y64, bound
 
     passes, t_cpu = 0, 0.0
-    y64 = bound = None
     while t_cpu < 10.0 and passes < 200:
-        a, b, y64, bound = phases(d, x, COLS)
+        a, b, _, _ = phases(d, x, COLS)
         t_cpu += a + b
         passes += 1
-    ratio = og.check(y_timed, y64, bound)
     one = []
     with threadpool_limits(limits=1):
         for _ in range(3):
@@ -729,8 +910,13 @@ def cpu_baseline(d, x, y_timed, per_shape):
         xx = synth.activations(cols, 1, cfg, rows=rows)
         ts = sorted(sum(phases(dd, xx, cols)[:2]) for _ in range(3))
         shapes["cfg%d_%dx%d" % (cfg, rows, cols)] = round(ts[1] * 1e6, 1)
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except AttributeError:
+        avail = os.cpu_count() or 1
     cpu = {"value": round(alg * passes / t_cpu / 1e9, 3), "unit": "GB/s",
-           "cores": int(threads), "kind": "oracle",
+           "cores": int(threads), "cores_available": int(avail), "kind": "oracle",
+           "value_1core": round(alg / (a1 + b1) / 1e9, 4),
            "sample": "the full 4096x12288 Leech matrix, f64 reconstruction + matvec + per-row "
                      "bound, %d passes in %.1fs (%.1f ms per GEMV)"
                      % (passes, t_cpu, 1e3 * t_cpu / passes),
@@ -738,7 +924,60 @@ def cpu_baseline(d, x, y_timed, per_shape):
            "oracle_us_ncores": {"reconstruct": round(many[0] * 1e6, 1),
                                 "matvec": round(many[1] * 1e6, 1)},
            "oracle_us_per_shape_ncores": shapes}
-    return cpu, ratio
+    return cpu
+
+
+# ---------------------------------------------------------------- streaming ceiling
+
+def ceiling_sweep(torch, lvq, args, nbytes):
+    """The fastest plain read of nbytes: every launch shape of
+    lvq_stream_read_geom (workgroup size, workgroups per CU or one trip per
+    thread, 16-byte loads in flight, non-temporal or ordinary loads) over the
+    same rotation of copies the GEMV records use, beside a device-to-device
+    copy of the same bytes (which also writes them) and the launch floor (a
+    read of nothing)."""
+    n = copies_for(nbytes)
+    stride = (nbytes + 255) // 256 * 256
+    buf = torch.empty((n, stride), dtype=torch.uint8, device="cuda")
+    buf.fill_(0x5A)
+    sink = torch.zeros(lvq.STREAM_GEOM_SINK_WORDS, dtype=torch.int32, device="cuda")
+    nb4 = nbytes // 4 * 4
+    rows = []
+
+    def timed(fn):
+        return Timed(torch, fn, args.steps, args.warmup, args.trials)
+
+    for threads in (256, 512, 1024):
+        for wpc in (0, 1, 2, 4, 8):
+            for unroll in (1, 2, 4, 8):
+                for nt in (1, 0):
+                    try:
+                        lvq.stream_read_geom(buf[0], nb4, sink, threads, wpc, unroll, nt)
+                    except lvq.LvqError:
+                        continue
+                    tm = timed(lambda i: lvq.stream_read_geom(buf[i % n], nb4, sink, threads,
+                                                              wpc, unroll, nt))
+                    rows.append({"threads": threads, "wgs_per_cu": wpc, "unroll": unroll,
+                                 "nontemporal": nt, "us": round(tm.median, 3),
+                                 "us_min": round(tm.us[0], 3)})
+                    log("read %4d thr %d/CU u%d nt%d: %.3f us" % (threads, wpc, unroll, nt,
+                                                                 tm.median))
+    floor = timed(lambda i: lvq.stream_read_geom(buf[0], 0, sink, 256, 1, 1, 1)).median
+    base = timed(lambda i: lvq.stream_read(buf[i % n], nb4, sink[:lvq.STREAM_SINK_WORDS])).median
+    dst = torch.empty((2, stride), dtype=torch.uint8, device="cuda")
+    cp = timed(lambda i: dst[i % 2].copy_(buf[i % n])).median
+    best = min(rows, key=lambda r: r["us"])
+    rec = {"arm": "stream_ceiling", "bytes": nbytes, "copies": n, "reps": args.steps,
+           "trials": args.trials, "sweep": rows, "best": best,
+           "best_gbps": round(nbytes / (best["us"] * 1e-6) / 1e9, 1),
+           "lvq_stream_read_us": round(base, 3), "launch_floor_us": round(floor, 3),
+           "d2d_copy_us": round(cp, 3),
+           "d2d_copy_gbps_read_plus_write": round(2 * nbytes / (cp * 1e-6) / 1e9, 1)}
+    log("ceiling over %d B: best %.3f us (%s), lvq_stream_read %.3f us, d2d copy %.3f us, "
+        "empty launch %.3f us" % (nbytes, best["us"], best, base, cp, floor))
+    del buf, dst
+    torch.cuda.empty_cache()
+    return rec
 
 
 # ---------------------------------------------------------------- main
@@ -819,18 +1058,42 @@ def main():
     if args.profile:
         profile_only(torch, lvq, args)
         return
+    if args.ceiling:
+        rec = ceiling_sweep(torch, lvq, args, args.ceiling_bytes or leech_bytes(ROWS, COLS))
+        rec.update({"device": props.name, "arch": arch, "torch": torch.__version__,
+                    "hip": getattr(torch.version, "hip", None)})
+        print(json.dumps(rec))
+        return
 
-    B = Bench(torch, lvq, args, props)
+    leg = OracleLeg(enabled=not args.no_cpu)
+    if not leg.enabled:
+        log("--no-cpu: the oracle leg is off, so no output is checked before it is timed")
+    B = Bench(torch, lvq, args, props, leg)
+    try:
+        out = run(torch, lvq, args, props, arch, B, leg, pool,
+                  stack_results if pool is not None else None,
+                  stack_jobs if pool is not None else 0)
+    except ParityGateError as e:
+        log("PARITY GATE FAILED, nothing is reported: %s" % e)
+        sys.exit(1)
+    finally:
+        if pool is not None:
+            pool.terminate()
+            pool.join()
+    print(json.dumps(out))
+
+
+def run(torch, lvq, args, props, arch, B, leg, pool, stack_results, stack_jobs):
     stack_blobs = None
     if pool is not None:
-        # the whole stack is drawn and on the device, and the workers are gone,
-        # before anything is timed: busy host cores would slow the enqueueing
+        # the whole stack is drawn and on the device before anything is
+        # timed (busy host cores would slow the enqueueing); the workers stay,
+        # idle, for the oracle leg's check of the stack
         stack_blobs = B.load_stack(stack_results, stack_jobs)
-        pool.close()
-        pool.join()
     t0 = time.perf_counter()
-    head, d, x, y_timed = B.leech(4, ROWS, COLS, 1, keep=True)
-    log("headline done in %.1fs" % (time.perf_counter() - t0))
+    head, d, x = B.leech(4, ROWS, COLS, 1, keep=True)
+    log("headline done in %.1fs (bit-exact decode %s, parity ratio %s)"
+        % (time.perf_counter() - t0, head.get("bitexact"), head.get("parity_max_ratio")))
 
     records = [head]
     stack = None
@@ -874,15 +1137,14 @@ def main():
             c = fp16_by_shape.get((r["R"], r["K"]))
             r["pct_fp16_control"] = round(100 * r["gbps"] / c, 1) if c and r["arm"] != "fp16" else None
         if stack_blobs is not None:
-            stack = B.stack(stack_blobs, args.stack_layers)
+            stack = B.stack(stack_blobs, args.stack_layers, pool)
             del stack_blobs
 
     cpu = None
     if not args.no_cpu:
         t0 = time.perf_counter()
-        cpu, ratio = cpu_baseline(d, x, y_timed, [(1, 1536, 1536), (3, 4096, 4096),
-                                                  (3, 12288, 4096), (3, 1024, 4096)])
-        head["parity_max_ratio"] = round(ratio, 5)
+        cpu = cpu_baseline(d, x, [(1, 1536, 1536), (3, 4096, 4096), (3, 12288, 4096),
+                                  (3, 1024, 4096)])
         head["oracle_us_1core"] = cpu["oracle_us_1core"]
         head["oracle_us_ncores"] = cpu["oracle_us_ncores"]
         head["ncores"] = cpu["cores"]
@@ -912,13 +1174,22 @@ def main():
                      "unit": "GB/s", "frac": round(value / HBM_PEAK_GBS, 4),
                      "traffic": traffic_from_profile()},
         "cpu_baseline": cpu,
-        "us_per_gemv": us,
-        "us_per_gemv_graph": getattr(B, "graph_us", None),
-        "pct_stream_ceiling": head["pct_stream_ceiling"],
         "records": records,
         "stack": stack,
+        # the summary last, so that the end of the line (what a log tail
+        # shows) carries the gate's verdict and the headline's context
+        "us_per_gemv": us,
+        "us_per_gemv_graph": getattr(B, "graph_us", None),
+        "us_noweights": head["us_noweights"],
+        "pct_stream_ceiling": head["pct_stream_ceiling"],
+        "cpu_cores_used": cpu["cores"] if cpu else None,
+        "cpu_cores_available": cpu["cores_available"] if cpu else None,
+        "parity_checks": len(leg.ratios),
+        "parity_max_ratio_all_records": leg.worst(),
+        "bitexact": head.get("bitexact"),
+        "parity_max_ratio": head.get("parity_max_ratio"),
     }
-    print(json.dumps(out))
+    return out
 
 
 if __name__ == "__main__":

@@ -87,6 +87,7 @@ def _load():
         "lvq_gemv_rotated": (i, [vp, i, i, vp, vp, i, vp, vp, i, vp]),
         "lvq_stream_read": (i, [vp, sz, vp, vp]),
         "lvq_stream_read_geom": (i, [vp, sz, vp, i, i, i, i, vp]),
+        "lvq_gemv_launch_info": (i, [i, i, i, i, i, vp]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -104,7 +105,7 @@ EXPORTED = ("lvq_strerror", "lvq_last_error_index", "lvq_class_table", "lvq_layo
             "lvq_rank", "lvq_gemv", "lvq_gemv_gain",
             "lvq_unfold", "lvq_gemv_fused", "lvq_gemv_noweights", "lvq_decode",
             "bpdq_gemv", "trellis_gemv", "fp16_gemv", "lvq_rotate", "lvq_gemv_rotated",
-            "lvq_stream_read", "lvq_stream_read_geom")
+            "lvq_stream_read", "lvq_stream_read_geom", "lvq_gemv_launch_info")
 
 
 def library():
@@ -396,3 +397,17 @@ def stream_read_geom(buf, nbytes: int, sink, threads: int, wgs_per_cu: int, unro
     _check(_lib.lvq_stream_read_geom(_ptr(buf), int(nbytes), _ptr(sink), int(threads),
                                      int(wgs_per_cu), int(unroll), int(bool(nontemporal)),
                                      _stream(stream)))
+
+
+LAUNCH_KINDS = {"gemv": 0, "rotated": 1, "direct": 2, "onehot": 3, "lp2": 4, "gain": 5,
+                "noweights": 6}
+
+
+def gemv_launch_info(kind: str, rows: int, cols: int, batch: int = 1, m: int = 1) -> dict:
+    """The launch a Leech GEMV entry point makes for this shape (nothing is
+    launched): threads, workgroups, blocks per lane, ring depth, LDS bytes."""
+    out = (ctypes.c_int * 5)()
+    _check(_lib.lvq_gemv_launch_info(LAUNCH_KINDS[kind], int(rows), int(cols), int(batch),
+                                     int(m), out))
+    return {"threads": out[0], "workgroups": out[1], "blocks_per_lane": out[2],
+            "ring": out[3], "lds_bytes": out[4]}

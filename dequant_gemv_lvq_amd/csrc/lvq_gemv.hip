@@ -1062,23 +1062,30 @@ int zero_output(float* y, size_t n, hipStream_t st) {
   return launch_status();
 }
 
-// Workgroups per CU that fit at once for a kernel, by the occupancy query,
-// cached per device and per (workgroup size, LDS above 64 KiB).  The cache
-// entries are ints written whole with the same value by any thread that
-// races on them.
+// Workgroups per CU that fit at once for one kernel, by the occupancy query,
+// kept in that kernel's own cache (`cache`, one per kernel instantiation) per
+// device and per (workgroup size, LDS above 64 KiB).  The entries are ints
+// written whole with the same value by any thread that races on them.
+typedef int OccupancyCache[kMaxDevices][3][2];
+
+// When set (lvq_gemv_launch_info), the Leech launch path records the launch
+// it would make here instead of making it.
+struct LaunchInfo {
+  int threads, workgroups, blocks_per_lane, ring, lds_bytes;
+};
+thread_local LaunchInfo* t_dry_run = nullptr;
 template <typename K>
-int wgs_per_cu(K kernel, int threads, size_t lds) {
-  static int cached[kMaxDevices][3][2];
+int wgs_per_cu(OccupancyCache& cache, K kernel, int threads, size_t lds) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) dev = 0;
   const int ti = threads == 1024 ? 0 : threads == 512 ? 1 : 2, li = lds > 64 * 1024;
-  int n = __atomic_load_n(&cached[dev][ti][li], __ATOMIC_RELAXED);
+  int n = __atomic_load_n(&cache[dev][ti][li], __ATOMIC_RELAXED);
   if (!n) {
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, threads, lds) != hipSuccess ||
         n < 1)
       n = 1;
     n = n > 2 ? 2 : n;
-    __atomic_store_n(&cached[dev][ti][li], n, __ATOMIC_RELAXED);
+    __atomic_store_n(&cache[dev][ti][li], n, __ATOMIC_RELAXED);
   }
   return n;
 }
@@ -1102,10 +1109,15 @@ int launch_leech_mode(const MatSet& ms, int rows, int cols, const uint16_t* x, h
   const int wpb = threads / kWave;
   // as many workgroups as fit on the chip at once (one or two per CU, by
   // registers and LDS), rows grid-strided over their waves
-  const int occ = wgs_per_cu(leech_gemv_kernel<B, BPL, M, D>, threads, lds);
+  static OccupancyCache occupancy;  // this instantiation's own
+  const int occ = wgs_per_cu(occupancy, leech_gemv_kernel<B, BPL, M, D>, threads, lds);
   long long wgs = ((long long)rows + wpb - 1) / wpb;
   if (wgs > (long long)occ * cus) wgs = (long long)occ * cus;
   if (wgs < 1) wgs = 1;
+  if (t_dry_run) {
+    *t_dry_run = {threads, (int)wgs, BPL, D, (int)lds};
+    return LVQ_OK;
+  }
   clear_hip_error();
   hipLaunchKernelGGL((leech_gemv_kernel<B, BPL, M, D>), dim3((unsigned)wgs), dim3(threads), lds,
                      st, ms, rows, nb, tau, cols, nchunks, (int)kpad, x);
@@ -1353,4 +1365,36 @@ extern "C" int lvq_decode(const void* blob, int rows, int cols, int8_t* coords_o
   hipLaunchKernelGGL(leech_decode_kernel, dim3((unsigned)((nblocks + 255) / 256)), dim3(256), 0,
                      (hipStream_t)stream, v, nblocks, coords_out);
   return launch_status();
+}
+
+// The launch a Leech GEMV entry point would make, without making it (see
+// include/lvq.h): the launch path runs with a thread-local record in place of
+// the launch, on fake 16-byte-aligned addresses that are never dereferenced.
+extern "C" int lvq_gemv_launch_info(int kind, int rows, int cols, int batch, int m,
+                                    int* info_out) {
+  if (!info_out) return LVQ_E_NULL;
+  if (rows < 1 || cols < 24) return LVQ_E_SHAPE;
+  static const int modes[] = {kSingle, kRot, kDirect, kOneHot, kLp2, kGain, kNoWeights};
+  if (kind < 0 || kind >= (int)(sizeof(modes) / sizeof(modes[0]))) return LVQ_E_SHAPE;
+  LaunchInfo info = {0, 0, 0, 0, 0};
+  t_dry_run = &info;
+  const uintptr_t fake = (uintptr_t)1 << 30;
+  const void* blob = (const void*)fake;
+  const uint16_t* x = (const uint16_t*)fake;
+  float* y = (float*)fake;
+  int e;
+  if (modes[kind] == kRot) {
+    e = lvq_gemv_rotated(blob, rows, cols, (const uint32_t*)fake, m > 1 ? (const float*)fake : nullptr,
+                         m, x, y, batch, nullptr);
+  } else {
+    e = single_gemv(blob, rows, cols, x, y, batch, nullptr, modes[kind]);
+  }
+  t_dry_run = nullptr;
+  if (e) return e;
+  info_out[0] = info.threads;
+  info_out[1] = info.workgroups;
+  info_out[2] = info.blocks_per_lane;
+  info_out[3] = info.ring;
+  info_out[4] = info.lds_bytes;
+  return LVQ_OK;
 }

@@ -1,6 +1,7 @@
 """The C ABI on the CPU: exports, the host expander against the oracle, and
 argument validation of the device entry points (which return before any HIP
 call, so no GPU is needed)."""
+import ctypes
 import os
 import re
 
@@ -9,6 +10,7 @@ import pytest
 from hypothesis import given, settings, strategies as st
 
 import dequant_gemv_lvq_amd as lvq
+import lattice_points
 import synth
 from oracle import golay, layout, leech
 
@@ -58,39 +60,8 @@ def _check_blob(coords, scale, tail, rows, cols):
     return blob, u
 
 
-def _shell2_vectors():
-    out = []
-    for i in range(24):
-        for j in range(i + 1, 24):
-            for si in (-4, 4):
-                for sj in (-4, 4):
-                    v = np.zeros(24, dtype=np.int8)
-                    v[i], v[j] = si, sj
-                    out.append(v)
-    octads = [int(w) for w in golay.codewords() if golay.weight(w) == 8]
-    for o in octads:
-        pos = [i for i in range(24) if (o >> i) & 1]
-        for s in range(256):
-            if bin(s).count("1") % 2:
-                continue
-            v = np.zeros(24, dtype=np.int8)
-            for t, p in enumerate(pos):
-                v[p] = -2 if (s >> t) & 1 else 2
-            out.append(v)
-    words = golay.codewords()
-    bits = ((words[:, None].astype(np.int64) >> np.arange(24)) & 1).astype(np.int8)
-    base = np.where(bits == 1, -1, 1).astype(np.int8)  # x = 3 mod 4 on the codeword
-    for p in range(24):
-        v = base.copy()
-        v[:, p] = np.where(bits[:, p] == 1, 3, -3)
-        out.extend(v)
-    x = np.array(out, dtype=np.int8)
-    x = x[leech.is_leech_batch(x)]
-    return x
-
-
 def test_expand_exhaustive_shell2():
-    x = _shell2_vectors()
+    x = lattice_points.shell2_vectors()
     assert x.shape[0] == 196560
     rows = 196560 // 24
     coords = x.reshape(rows, 24, 24)
@@ -181,6 +152,42 @@ def test_device_entry_points_validate_before_launch():
     assert lib.lvq_stream_read(A, 64, None, None) == lvq.LVQ_E_NULL
     assert lib.lvq_stream_read(A + 4, 64, A, None) == lvq.LVQ_E_ALIGN
     assert lib.lvq_stream_read(A, 66, A, None) == lvq.LVQ_E_ALIGN
+    assert lib.lvq_stream_read_geom(None, 64, A, 256, 1, 1, 1, None) == lvq.LVQ_E_NULL
+    assert lib.lvq_stream_read_geom(A + 4, 64, A, 256, 1, 1, 1, None) == lvq.LVQ_E_ALIGN
+    assert lib.lvq_stream_read_geom(A, 64, A, 128, 1, 1, 1, None) == lvq.LVQ_E_SHAPE
+    assert lib.lvq_stream_read_geom(A, 64, A, 256, 9, 1, 1, None) == lvq.LVQ_E_SHAPE
+    assert lib.lvq_stream_read_geom(A, 64, A, 256, 1, 3, 1, None) == lvq.LVQ_E_SHAPE
+    # one trip per thread over 2^31 bytes at 256 x 1 loads needs 524,288
+    # workgroups, more than the sink holds: refused before any launch
+    assert lib.lvq_stream_read_geom(A, 1 << 31, A, 256, 0, 1, 1, None) == lvq.LVQ_E_SHAPE
+
+
+@pytest.mark.parametrize("name", ["expand", "expand_lp2", "expand_lp2x", "expand_direct",
+                                  "expand_onehot", "expand_gain"])
+def test_expanders_reject_short_host_arrays(name):
+    """Every host expander checks the sizes of coords, scale and tail before
+    the native call, so a short array is refused instead of read past."""
+    rows, cols = 3, 74  # two blocks and a tail of 2 per row
+    d = synth.leech_matrix(rows, cols, 3, key=(5,))
+    fn = getattr(lvq, name)
+
+    def call(coords, scale, tail):
+        if name == "expand_gain":
+            return fn(coords, np.zeros((rows, cols // 24), np.uint8), scale, tail, rows, cols)
+        return fn(coords, scale, tail, rows, cols)
+
+    call(d["coords"], d["scale"], d["tail"])  # the full arrays are accepted
+    bad = [(d["coords"][:2], d["scale"], d["tail"]),
+           (d["coords"], d["scale"][:2], d["tail"]),
+           (d["coords"], d["scale"], d["tail"][:2]),
+           (d["coords"], d["scale"], None)]
+    for coords, scale, tail in bad:
+        with pytest.raises(lvq.LvqError) as e:
+            call(coords, scale, tail)
+        assert e.value.code == lvq.LVQ_E_SHAPE
+    if name == "expand_gain":
+        with pytest.raises(lvq.LvqError):
+            fn(d["coords"], np.zeros(rows, np.uint8), d["scale"], d["tail"], rows, cols)
 
 
 def test_fused_and_noweights_validate_before_launch():
@@ -539,3 +546,25 @@ def test_gemv_onehot_validates_before_launch():
     with pytest.raises(lvq.LvqError) as e:
         lvq.expand_onehot(x, synth.fp16_bits([1.0]), None, 1, 24)
     assert e.value.code == lvq.LVQ_E_NOT_LEECH and e.value.index == (0, 0)
+
+
+def test_launch_info_rules_and_validation():
+    """The launch the Leech entry points make (nothing is launched): one block
+    per lane and a ring of three on rows of two or three 64-block chunks, two
+    blocks per lane and a ring of two at 4096 x 12288; LDS = class table + x."""
+    lib = lvq.library()
+    out = (ctypes.c_int * 5)()
+    assert lib.lvq_gemv_launch_info(0, 16, 48, 1, 1, None) == lvq.LVQ_E_NULL
+    assert lib.lvq_gemv_launch_info(99, 16, 48, 1, 1, out) == lvq.LVQ_E_SHAPE
+    assert lib.lvq_gemv_launch_info(0, 0, 48, 1, 1, out) == lvq.LVQ_E_SHAPE
+    assert lib.lvq_gemv_launch_info(0, 16, 48, 5, 1, out) == lvq.LVQ_E_BATCH
+    assert lib.lvq_gemv_launch_info(1, 16, 48, 1, 5, out) == lvq.LVQ_E_SHAPE  # 48 % 5
+    head = lvq.gemv_launch_info("gemv", 4096, 12288)
+    assert (head["blocks_per_lane"], head["ring"]) == (2, 2)
+    assert head["lds_bytes"] == 302 * 8 + 12288 * 2
+    for rows in (4096, 12288):
+        short = lvq.gemv_launch_info("gemv", rows, 4096)
+        assert (short["blocks_per_lane"], short["ring"]) == (1, 3)
+    # the fused rotation and few rows keep the blocks-per-lane rule
+    assert lvq.gemv_launch_info("rotated", 12288, 4096)["ring"] == 2
+    assert lvq.gemv_launch_info("gemv", 1024, 4096)["ring"] == 2

@@ -46,3 +46,21 @@ def test_row_results_do_not_depend_on_the_launch(rows, cols, batch, layout):
         assert np.array_equal(part.view(np.uint32), full[:, :k].view(np.uint32)), (k, layout)
     print("%s %dx%d b%d: first 40 and 2500 rows equal the full launch bit for bit" % (
         layout, rows, cols, batch), flush=True)
+
+
+def test_each_kernel_keeps_its_own_occupancy():
+    """The grid of a launch comes from the occupancy of that kernel: after a
+    plain GEMV (two 1024-thread workgroups per CU) has been sized, the fused
+    rotation at the same shape (more registers: one workgroup per CU) must
+    still get its own, smaller grid.  A cache shared by all kernel variants
+    once gave it the plain kernel's grid, half of which then waited for a
+    second round (15.5 instead of 11.7 us at 12288 x 4096)."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    plain = lvq.gemv_launch_info("gemv", 12288, 4096)
+    rot = lvq.gemv_launch_info("rotated", 12288, 4096)
+    b4 = lvq.gemv_launch_info("gemv", 12288, 4096, batch=4)
+    assert plain["threads"] == rot["threads"] == 1024
+    assert plain["workgroups"] == 2 * cus
+    assert rot["workgroups"] == cus
+    assert b4["workgroups"] == cus  # batch 4: more registers, one per CU
+    assert lvq.gemv_launch_info("gemv", 12288, 4096)["workgroups"] == 2 * cus
