@@ -12,7 +12,8 @@
 // and x into LDS with buffer loads that write LDS directly, then its waves
 // walk rows (one row per wave at a time).  Lane l takes code words l, l + 64,
 // ... of the row; all of them are requested at once, so a row costs one
-// memory round trip.  The word before word w in its packet (w - 1, or the
+// memory round trip, and a wave's first row is requested before the staging
+// barrier, so that round trip overlaps the 128 KiB table copy.  The word before word w in its packet (w - 1, or the
 // packet's last word for its first word) is held by lane l - 1 or l + 15 and
 // comes over with one lane shuffle.  For each of the 16 symbols of a word the
 // table's byte address (state * 2) is one funnel shift of the previous and
@@ -54,42 +55,63 @@ trellis_gemv_kernel(const uint32_t* __restrict__ bits, const uint16_t* __restric
                     const uint16_t* __restrict__ scale, int rows, int cols,
                     const uint16_t* __restrict__ x, float* __restrict__ y) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  // smem: the table fp16 [65536] (byte address 2 * state), then x
-  uint32_t* xs = (uint32_t*)(smem + 65536 * 2);    // [B][cols/2] natural-order pairs
+  // smem: the table fp16 [65536] (byte address 2 * state), then x as
+  // [B][2][nw] 16-byte units: unit (h, w) holds the pairs 4h .. 4h + 3 of
+  // code word w's 16 columns, so the lanes of a wave (consecutive words)
+  // read consecutive units
+  uint32_t* xs = (uint32_t*)(smem + 65536 * 2);
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int nw = cols / 16;
 
-  // table and x straight into LDS, 1 KiB per wave instruction
+  const int wave = blockIdx.x * kTrellisWaves + wv;
+  const int nwaves = gridDim.x * kTrellisWaves;
+  // one row's code words (every word at once; words past the row's end, or
+  // a row past the last, read 0) and its scale
+  uint32_t cw[kTrellisMaxWordsPerLane];
+  uint32_t sbits = 0;
+  auto load_row = [&](int r) {
+    const bool ok = r < rows;
+    const auto rb = trellis_rsrc(bits + (size_t)(ok ? r : 0) * nw, ok ? (uint32_t)nw * 4 : 0u);
+    // no branch per load (a load past the row's range reads 0 and makes no
+    // request), so the waits after it count exactly
+#pragma unroll
+    for (int j = 0; j < kTrellisMaxWordsPerLane; ++j)
+      cw[j] = __builtin_amdgcn_raw_buffer_load_b32(rb, (lane + j * kWave) * 4, 0, 2);
+    const auto rsc = trellis_rsrc(scale + (ok ? r : 0), ok ? 2u : 0u);
+    sbits = __builtin_amdgcn_raw_buffer_load_b16(rsc, 0, 0, 0);
+  };
+
+  // table and x straight into LDS, 1 KiB per wave instruction; the first
+  // row's code words are requested right behind them, so they arrive while
+  // the table is copied (the barrier waits for the copies only)
   {
     const auto rt = trellis_rsrc(table, 65536 * 2);
     for (int q = wv; q < 128; q += kTrellisWaves)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           rt, (__attribute__((address_space(3))) void*)(smem + q * 1024), 16, lane * 16, q * 1024,
           0, 0);
+    // each lane of a copy fetches the natural unit its transposed LDS unit
+    // holds (units past x read 0)
     const int xbytes = B * cols * 2;  // a multiple of 512
+    const int units = 2 * nw;         // 16-byte units per batch row
     const auto rx = trellis_rsrc(x, (uint32_t)xbytes);
-    for (int q = wv; q * 1024 < xbytes; q += kTrellisWaves)
+    for (int q = wv; q * 1024 < xbytes; q += kTrellisWaves) {
+      const int u = q * kWave + lane, bb = u / units, k = u - bb * units;
+      const int h = k >= nw ? 1 : 0, w = k - h * nw;
+      const int src = u < B * units ? (bb * units + 2 * w + h) * 16 : xbytes;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rx, (__attribute__((address_space(3))) void*)((uint8_t*)xs + q * 1024), 16, lane * 16,
-          q * 1024, 0, 0);
+          rx, (__attribute__((address_space(3))) void*)((uint8_t*)xs + q * 1024), 16, src, 0, 0,
+          0);
+    }
   }
+  load_row(wave);
   __syncthreads();
 
-  const int wave = blockIdx.x * kTrellisWaves + wv;
-  const int nwaves = gridDim.x * kTrellisWaves;
   const int src = (lane & 15) ? lane - 1 : lane + 15;  // holder of the previous word
   for (int r = wave; r < rows; r += nwaves) {
-    // every word of the row at once (words past the row's end read 0)
-    const auto rb = trellis_rsrc(bits + (size_t)r * nw, (uint32_t)nw * 4);
-    uint32_t cw[kTrellisMaxWordsPerLane];
-#pragma unroll
-    for (int j = 0; j < kTrellisMaxWordsPerLane; ++j)
-      cw[j] = j * kWave < nw ? __builtin_amdgcn_raw_buffer_load_b32(rb, (lane + j * kWave) * 4, 0, 2)
-                             : 0u;
-    const auto rsc = trellis_rsrc(scale + r, 2);
-    const uint32_t sbits = __builtin_amdgcn_raw_buffer_load_b16(rsc, 0, 0, 0);
+    if (r != wave) load_row(r);
     float acc[B][2];
 #pragma unroll
     for (int bb = 0; bb < B; ++bb) acc[bb][0] = acc[bb][1] = 0.f;
@@ -108,9 +130,12 @@ trellis_gemv_kernel(const uint32_t* __restrict__ bits, const uint16_t* __restric
           h.y = *lds_f16(trellis_addr(prev, cur, p + 1));
           const uint32_t w2 = __builtin_bit_cast(uint32_t, h);
 #pragma unroll
-          for (int bb = 0; bb < B; ++bb)
-            acc[bb][(p >> 1) & 1] =
-                dot2(w2, xs[(size_t)bb * (cols / 2) + 8 * w + (p >> 1)], acc[bb][(p >> 1) & 1]);
+          for (int bb = 0; bb < B; ++bb) {
+            const int pr = p >> 1;  // pair 0..7 of the word's 16 columns
+            acc[bb][pr & 1] = dot2(
+                w2, xs[(size_t)bb * (cols / 2) + ((pr >> 2) * nw + w) * 4 + (pr & 3)],
+                acc[bb][pr & 1]);
+          }
         }
       }
     }
