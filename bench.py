@@ -28,8 +28,9 @@ kernel at these shapes is the GPU test suite's job; the cpu_baseline leg,
 which runs the oracle on the timed workload anyway, also reports the largest
 error ratio of the timed Leech output.
 
---profile KERNEL runs only that kernel's launch loop (for rocprofv3 counters;
-the Leech kinds at 4096 x 12288, batch --profile-batch);
+--profile KERNEL runs only that kernel's timed launches (for rocprofv3: the
+same warm-up and trials of back-to-back launches; the Leech kinds at
+4096 x 12288, batch --profile-batch);
 --profile copy runs a plain fp32->fp16 conversion of known size, the
 reference that scales the FETCH_SIZE / WRITE_SIZE counters to bytes.
 """
@@ -1029,10 +1030,12 @@ def profile_only(torch, lvq, args):
         xd = to_dev(torch, synth.activations(COLS, 1, 4, rows=ROWS))
         yd = torch.empty((1, ROWS), dtype=torch.float32, device="cuda")
         fn = lambda i: lvq.trellis_gemv(bits[i % n], table, scale, ROWS, COLS, xd, yd, 1)  # noqa
-    for i in range(steps):
-        fn(i)
-    torch.cuda.synchronize()
-    log("profile %s: %d launches" % (args.profile, steps))
+    # the bench's protocol: warm-up, then trials of back-to-back launches
+    # enqueued behind a spin kernel, so the GPU runs them without gaps (a
+    # profiler's per-dispatch times then match the bench's events)
+    tm = Timed(torch, fn, steps, args.warmup, args.trials)
+    log("profile %s: %d warm-up + %d x %d launches, median %.3f us per launch"
+        % (args.profile, args.warmup, args.trials, steps, tm.median))
 
 
 def main():
