@@ -9,40 +9,42 @@
 // plane i selects, and a deterministic split over K.
 //
 // gfx950 design.  The layout puts consecutive rows in consecutive words, so a
-// lane is a (row, quarter group) pair: a 1024-thread workgroup covers 16 rows
-// x 64 quarter groups of 64 columns (4 code words each); every load
-// instruction of a wave reads four 64-byte runs (16 rows of 4 quarter
-// groups).  The form is linear, so each lane applies its group's coefficients
-// to its own quarter: c0 * S0q + c1 * S1q + c2 * Xq, with Xq the sum of x over
-// the quarter.  Bits are never shifted into place: a mask keeps bit 2c (plane
-// 0) or 2c+1 (plane 1) of the columns c and c+8 of a word, and that masked
-// word, read as two fp16 subnormals (2^(2c) or 2^(2c+1) times 2^-24), goes
-// straight into v_dot2_f32_f16 against the x pair (x_c, x_{c+8}); columns
-// 5..7 use the word shifted right by 10.  Ten fp32 accumulators (2 planes x 5
-// powers of two) are rescaled exactly at the end of each quarter.  x pairs
-// and quarter sums are staged in LDS once per workgroup; the 64 partials of a
-// row are summed by shuffles inside a wave and then over the 16 waves in LDS,
-// always in the same order.  Neighbouring 16-row tiles share 128-byte lines
-// and are mapped to workgroups on the same XCD.
+// lane is a (row, unit) pair, a unit being U consecutive code words (16 U
+// columns, a quarter or a half of a group): a workgroup covers 16 rows x
+// SLOTS units, every load instruction of a wave reads four 64-byte runs (16
+// rows of 4 units), and a lane walks its units SLOTS apart, the next unit's
+// words requested while the current one is summed.  The form is linear, so
+// each lane applies its group's coefficients to its own unit:
+// c0 * S0u + c1 * S1u + c2 * Xu, with Xu the sum of x over the unit.  Bits
+// are never shifted into place: a mask keeps bit 2c (plane 0) or 2c+1 (plane
+// 1) of the columns c and c+8 of a word, and that masked word, read as two
+// fp16 subnormals (2^(2c) or 2^(2c+1) times 2^-24), goes straight into
+// v_dot2_f32_f16 against the x pair (x_c, x_{c+8}); columns 5..7 use the word
+// shifted right by 10.  Ten fp32 accumulators per batch row (2 planes x 5
+// powers of two) are rescaled exactly at the end of each unit.  x pairs and
+// unit sums are staged in LDS once per workgroup, the x words requested
+// before the code words so the copy runs under their latency; the SLOTS
+// partials of a row are summed by shuffles inside a wave and then over the
+// waves in LDS, always in the same order.  Neighbouring 16-row tiles share
+// 128-byte lines and are mapped to workgroups on the same XCD.
 
 #include "common.h"
 
 namespace lvq {
 
-constexpr int kBpdqThreads = 1024;
 constexpr int kBpdqRows = 16;
-constexpr int kBpdqWaves = kBpdqThreads / kWave;
-constexpr int kBpdqSlices = kBpdqWaves * (kWave / kBpdqRows);  // 64 quarter-group slots
 
-template <int B>
-__global__ void __launch_bounds__(kBpdqThreads)
+template <int B, int U, int SLOTS>
+__global__ void __launch_bounds__(kBpdqRows * SLOTS)
 bpdq_gemv_kernel(const uint32_t* __restrict__ codes, const uint16_t* __restrict__ coeffs,
                  int rows, int cols, const uint16_t* __restrict__ x, float* __restrict__ y) {
+  static_assert(U == 4 || U == 8 || U == 16, "a unit is a quarter, half or whole group");
+  constexpr int kThreads = kBpdqRows * SLOTS, kWaves = kThreads / kWave;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  const int nwords = cols / 16, Q = cols / 64;
+  const int nwords = cols / 16, nunits = nwords / U;
   uint32_t* xp = (uint32_t*)smem;                          // [B][nwords][8] pairs
-  float* xq = (float*)(xp + (size_t)B * nwords * 8);       // [B][Q] quarter sums
-  float* red = xq + (size_t)B * Q;                         // [16 waves][16 rows][B]
+  float* xu = (float*)(xp + (size_t)B * nwords * 8);       // [B][nunits] unit sums
+  float* red = xu + (size_t)B * nunits;                    // [waves][16 rows][B]
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -51,26 +53,55 @@ bpdq_gemv_kernel(const uint32_t* __restrict__ codes, const uint16_t* __restrict_
   int tile = blockIdx.x;
   if ((ntiles & 7) == 0) tile = (blockIdx.x & 7) * (ntiles >> 3) + (blockIdx.x >> 3);
   const int ir = lane & (kBpdqRows - 1);
-  const int slice = wave * (kWave / kBpdqRows) + (lane >> 4);
+  const int slot = wave * (kWave / kBpdqRows) + (lane >> 4);
   const int r = tile * kBpdqRows + ir;
   const int rr = r < rows ? r : rows - 1;  // loads stay in bounds; the row is dropped at the end
 
-  // 1. this lane's first quarter: code words and coefficients, requested first
-  uint32_t u[4];
-  uint16_t cf[3];
-  auto load_q = [&](int q) {
+  // 1. this thread's first B x words (16 columns each), requested first: the
+  //    copy into LDS is what the barrier waits for.  A word past the end
+  //    reads word 0 and stores nothing.
+  const int nst = B * nwords;
+  uint4 xlo[B], xhi[B];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) u[j] = __builtin_nontemporal_load(codes + (size_t)(4 * q + j) * rows + rr);
-    const int g = q >> 2;
-#pragma unroll
-    for (int i = 0; i < 3; ++i) cf[i] = coeffs[((size_t)g * 3 + i) * rows + rr];
-  };
-  if (slice < Q) load_q(slice);
+  for (int k = 0; k < B; ++k) {
+    const int i = tid + k * kThreads;
+    const uint4* xs = (const uint4*)(x + (size_t)(i < nst ? i : 0) * 16);
+    xlo[k] = xs[0];  // columns 0..7
+    xhi[k] = xs[1];  // columns 8..15
+  }
 
-  // 2. x pairs (x_c, x_{c+8}) per code word, and quarter sums, in LDS
-  for (int i = tid; i < B * nwords; i += kBpdqThreads) {
-    const uint4* s = (const uint4*)(x + (size_t)i * 16);  // batch rows are contiguous
-    const uint4 lo = s[0], hi = s[1];                      // columns 0..7 and 8..15
+  // 2. this lane's first unit: code words and coefficients.  Raw buffer
+  //    loads: the lane's offset is computed once per unit and the word j and
+  //    coefficient i steps are scalar offsets, so no vector instruction goes
+  //    to 64-bit addressing.  A unit past the row's end gets an offset past
+  //    the buffer, which the hardware answers with zeros and no request; the
+  //    loads stay branch-free, so every later wait counts exactly them.
+  uint32_t u[U];
+  uint16_t cf[3];
+  const uint32_t code_bytes = (uint32_t)nwords * rows * 4;
+  const auto rcodes = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t*>(codes), (short)0,
+                                                        (int)code_bytes, 0x00020000);
+  const auto rcoef = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(coeffs), (short)0,
+                                                       (int)((uint32_t)(cols / 256) * 3 * rows * 2),
+                                                       0x00020000);
+  auto load_unit = [&](int n) {
+    const bool ok = n < nunits;
+    const int vo = ok ? (U * n * rows + rr) * 4 : (int)code_bytes;
+#pragma unroll
+    for (int j = 0; j < U; ++j)
+      u[j] = __builtin_amdgcn_raw_buffer_load_b32(rcodes, vo, j * rows * 4, 2);
+    const int vc = ok ? ((n * U / 16) * 3 * rows + rr) * 2 : (int)code_bytes;
+#pragma unroll
+    for (int i = 0; i < 3; ++i) cf[i] = __builtin_amdgcn_raw_buffer_load_b16(rcoef, vc, i * rows * 2, 0);
+  };
+  load_unit(slot);
+
+  // 3. x pairs (x_c, x_{c+8}) of each code word, and the sum of x over each
+  //    unit, into LDS.  The thread that pairs a word also sums its 16 values
+  //    (v_dot2 against (1, 1), fixed order); the U words of a unit sit in U
+  //    neighbouring lanes of one DPP row and are added by quad swaps and
+  //    mirrors, the same operands on every lane.
+  auto stage = [&](int i, uint4 lo, uint4 hi) {
     const uint32_t a[4] = {lo.x, lo.y, lo.z, lo.w}, b[4] = {hi.x, hi.y, hi.z, hi.w};
     uint32_t p[8];
 #pragma unroll
@@ -78,77 +109,88 @@ bpdq_gemv_kernel(const uint32_t* __restrict__ codes, const uint16_t* __restrict_
       p[2 * k] = __builtin_amdgcn_perm(b[k], a[k], 0x05040100u);      // x_{2k}, x_{2k+8}
       p[2 * k + 1] = __builtin_amdgcn_perm(b[k], a[k], 0x07060302u);  // x_{2k+1}, x_{2k+9}
     }
-    uint4* d = (uint4*)(xp + (size_t)i * 8);
-    d[0] = make_uint4(p[0], p[1], p[2], p[3]);
-    d[1] = make_uint4(p[4], p[5], p[6], p[7]);
-  }
-  {
-    // 16 threads per quarter (4 columns each), summed in a fixed tree
-    const int nq = B * Q;
-    for (int base = 0; base < nq * 16; base += kBpdqThreads) {
-      const int i = base + tid, q = i >> 4, part = i & 15;
-      float s = 0.f;
-      if (q < nq) {
-        const uint2 v = *(const uint2*)(x + (size_t)q * 64 + 4 * part);
-        s = (float)__builtin_bit_cast(_Float16, (uint16_t)v.x) +
-            (float)__builtin_bit_cast(_Float16, (uint16_t)(v.x >> 16));
-        s += (float)__builtin_bit_cast(_Float16, (uint16_t)v.y) +
-             (float)__builtin_bit_cast(_Float16, (uint16_t)(v.y >> 16));
-      }
-#pragma unroll
-      for (int off = 1; off < 16; off <<= 1) s += __shfl_xor(s, off, kWave);
-      if (q < nq && part == 0) xq[q] = s;
+    constexpr uint32_t kOnes = 0x3C003C00u;  // (1.0, 1.0)
+    float s = (dot2(a[1], kOnes, dot2(a[0], kOnes, 0.f)) +
+               dot2(a[3], kOnes, dot2(a[2], kOnes, 0.f))) +
+              (dot2(b[1], kOnes, dot2(b[0], kOnes, 0.f)) +
+               dot2(b[3], kOnes, dot2(b[2], kOnes, 0.f)));
+    s = dpp_add<0x4E, 0xF>(dpp_add<0xB1, 0xF>(s));  // quad_perm swaps: 4 words
+    if (U >= 8) s = dpp_add<0x141, 0xF>(s);          // row_half_mirror: 8 words
+    if (U >= 16) s = dpp_add<0x140, 0xF>(s);         // row_mirror: 16 words
+    if (i < nst) {
+      uint4* d = (uint4*)(xp + (size_t)i * 8);
+      d[0] = make_uint4(p[0], p[1], p[2], p[3]);
+      d[1] = make_uint4(p[4], p[5], p[6], p[7]);
+      if (i % U == 0) xu[i / U] = s;  // word i of batch row bb: unit bb * nunits + w / U
     }
+  };
+#pragma unroll
+  for (int k = 0; k < B; ++k) stage(tid + k * kThreads, xlo[k], xhi[k]);
+  for (int i = tid + B * kThreads; i < nst; i += kThreads) {
+    const uint4* xs = (const uint4*)(x + (size_t)i * 16);
+    stage(i, xs[0], xs[1]);
   }
   __syncthreads();
 
-  // 3. quarters of this lane's row
+  // 4. units of this lane's row.  Per code word the 16 masked operands are
+  //    formed once and used by every batch row.
   float acc[B];
 #pragma unroll
   for (int bb = 0; bb < B; ++bb) acc[bb] = 0.f;
-  for (int q = slice; q < Q; q += kBpdqSlices) {
+  for (int n = slot; n < nunits; n += SLOTS) {
     const float c0 = (float)__builtin_bit_cast(_Float16, cf[0]);
     const float c1 = (float)__builtin_bit_cast(_Float16, cf[1]);
     const float c2 = (float)__builtin_bit_cast(_Float16, cf[2]);
-    uint32_t w[4];
+    uint32_t w[U];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) w[j] = u[j];
-    if (q + kBpdqSlices < Q) load_q(q + kBpdqSlices);  // the next quarter, if any
-    // one batch row at a time: ten accumulators live, not ten per row
+    for (int j = 0; j < U; ++j) w[j] = u[j];
+    load_unit(n + SLOTS);  // the next unit, or nothing past the row
+    float a0[B][5], a1[B][5];
 #pragma unroll
-    for (int bb = 0; bb < B; ++bb) {
-      float a0[5], a1[5];
+    for (int bb = 0; bb < B; ++bb)
 #pragma unroll
-      for (int e = 0; e < 5; ++e) a0[e] = a1[e] = 0.f;
+      for (int e = 0; e < 5; ++e) a0[bb][e] = a1[bb][e] = 0.f;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uint32_t wj = w[j], w10 = wj >> 10;
-        const uint4* xw = (const uint4*)(xp + ((size_t)bb * nwords + 4 * q + j) * 8);
+    for (int j = 0; j < U; ++j) {
+      const uint32_t wj = w[j], w10 = wj >> 10;
+      uint32_t m0[8], m1[8];
+#pragma unroll
+      for (int c = 0; c < 5; ++c) {
+        m0[c] = wj & (0x00010001u << (2 * c));
+        m1[c] = wj & (0x00020002u << (2 * c));
+      }
+#pragma unroll
+      for (int c = 0; c < 3; ++c) {
+        m0[c + 5] = w10 & (0x00010001u << (2 * c));
+        m1[c + 5] = w10 & (0x00020002u << (2 * c));
+      }
+#pragma unroll
+      for (int bb = 0; bb < B; ++bb) {
+        const uint4* xw = (const uint4*)(xp + ((size_t)bb * nwords + U * n + j) * 8);
         const uint4 xa = xw[0], xb = xw[1];
         const uint32_t xv[8] = {xa.x, xa.y, xa.z, xa.w, xb.x, xb.y, xb.z, xb.w};
 #pragma unroll
-        for (int c = 0; c < 5; ++c) {
-          a0[c] = dot2(wj & (0x00010001u << (2 * c)), xv[c], a0[c]);
-          a1[c] = dot2(wj & (0x00020002u << (2 * c)), xv[c], a1[c]);
-        }
-#pragma unroll
-        for (int c = 0; c < 3; ++c) {
-          a0[c] = dot2(w10 & (0x00010001u << (2 * c)), xv[c + 5], a0[c]);
-          a1[c] = dot2(w10 & (0x00020002u << (2 * c)), xv[c + 5], a1[c]);
+        for (int c = 0; c < 8; ++c) {
+          const int e = c < 5 ? c : c - 5;  // columns 5..7 ride at the powers of 0..2
+          a0[bb][e] = dot2(m0[c], xv[c], a0[bb][e]);
+          a1[bb][e] = dot2(m1[c], xv[c], a1[bb][e]);
         }
       }
+    }
+#pragma unroll
+    for (int bb = 0; bb < B; ++bb) {
       float s0 = 0.f, s1 = 0.f;
 #pragma unroll
       for (int e = 0; e < 5; ++e) {
         const float sc = (float)(1u << (24 - 2 * e));  // exact powers of two
-        s0 += a0[e] * sc;
-        s1 += a1[e] * (sc * 0.5f);
+        s0 += a0[bb][e] * sc;
+        s1 += a1[bb][e] * (sc * 0.5f);
       }
-      acc[bb] += c0 * s0 + c1 * s1 + c2 * xq[bb * Q + q];
+      acc[bb] += c0 * s0 + c1 * s1 + c2 * xu[bb * nunits + n];
     }
   }
 
-  // 4. fixed-order reduction: the 4 quarter slots of a wave, then 16 waves
+  // 5. fixed-order reduction: the 4 unit slots of a wave, then the waves
 #pragma unroll
   for (int bb = 0; bb < B; ++bb) {
     float v = acc[bb];
@@ -161,24 +203,60 @@ bpdq_gemv_kernel(const uint32_t* __restrict__ codes, const uint16_t* __restrict_
     const int row = tid / B, bb = tid - row * B;
     const int rg = tile * kBpdqRows + row;
     float s = 0.f;
-    for (int wv = 0; wv < kBpdqWaves; ++wv) s += red[(wv * kBpdqRows + row) * B + bb];
+    for (int wv = 0; wv < kWaves; ++wv) s += red[(wv * kBpdqRows + row) * B + bb];
     if (rg < rows) y[(size_t)bb * rows + rg] = s;
   }
 }
 
 int zero_output(float* y, size_t n, hipStream_t st);
 
-template <int B>
+template <int B, int U, int SLOTS>
 int launch_bpdq(const uint32_t* codes, const uint16_t* coeffs, int rows, int cols,
                 const uint16_t* x, float* y, hipStream_t st) {
-  const size_t lds = (size_t)B * cols * 2 + (size_t)B * (cols / 64) * 4 +
-                     (size_t)kBpdqWaves * kBpdqRows * B * 4;
+  constexpr int kThreads = kBpdqRows * SLOTS;
+  const size_t lds = (size_t)B * cols * 2 + (size_t)B * (cols / (16 * U)) * 4 +
+                     (size_t)(kThreads / kWave) * kBpdqRows * B * 4;
   if (lds > device_lds_bytes()) return LVQ_E_SHAPE;
   const int ntiles = (rows + kBpdqRows - 1) / kBpdqRows;
   clear_hip_error();
-  hipLaunchKernelGGL(bpdq_gemv_kernel<B>, dim3(ntiles), dim3(kBpdqThreads), lds, st, codes, coeffs,
-                     rows, cols, x, y);
+  hipLaunchKernelGGL((bpdq_gemv_kernel<B, U, SLOTS>), dim3(ntiles), dim3(kThreads), lds, st,
+                     codes, coeffs, rows, cols, x, y);
   return launch_status();
+}
+
+// Lane shapes (unit words, slots), most slots first.  Each lane takes about
+// two units, the next unit's words requested while the current one is summed:
+// the fewest units per lane that is at least two, else the most; ties go to
+// more slots (more waves).  At 4096 x 4096 that is quarters, 32 slots (two
+// waves per SIMD); at 4096 x 12288 quarters, 64 slots, three per lane.
+struct BpdqShape {
+  int unit, slots;
+};
+constexpr BpdqShape kBpdqShapes[] = {{4, 64}, {8, 32}, {4, 32}, {8, 16}};
+constexpr int kNumBpdqShapes = sizeof(kBpdqShapes) / sizeof(kBpdqShapes[0]);
+
+inline int bpdq_shape(int cols) {
+  int best = -1, bk = 0;
+  for (int i = 0; i < kNumBpdqShapes; ++i) {
+    const int nunits = cols / 16 / kBpdqShapes[i].unit;
+    const int k = (nunits + kBpdqShapes[i].slots - 1) / kBpdqShapes[i].slots;
+    if (best < 0 || (k >= 2 ? (bk < 2 || k < bk) : (bk < 2 && k > bk))) {
+      best = i;
+      bk = k;
+    }
+  }
+  return best;
+}
+
+template <int B>
+int launch_bpdq_batch(const uint32_t* codes, const uint16_t* coeffs, int rows, int cols,
+                      const uint16_t* x, float* y, hipStream_t st) {
+  switch (bpdq_shape(cols)) {
+    case 0: return launch_bpdq<B, 4, 64>(codes, coeffs, rows, cols, x, y, st);
+    case 1: return launch_bpdq<B, 8, 32>(codes, coeffs, rows, cols, x, y, st);
+    case 2: return launch_bpdq<B, 4, 32>(codes, coeffs, rows, cols, x, y, st);
+    default: return launch_bpdq<B, 8, 16>(codes, coeffs, rows, cols, x, y, st);
+  }
 }
 
 }  // namespace lvq
@@ -193,13 +271,14 @@ extern "C" int bpdq_gemv(const uint32_t* codes, const uint16_t* coeffs, int rows
   if (!y || (rows && cols && (!codes || !coeffs || !x))) return LVQ_E_NULL;
   if (!aligned16(codes) || !aligned16(coeffs) || !aligned16(x) || !aligned16(y)) return LVQ_E_ALIGN;
   if ((long long)batch * cols > 65536) return LVQ_E_SHAPE;
+  if ((long long)rows * cols / 4 > INT32_MAX) return LVQ_E_SHAPE;  // 32-bit buffer offsets
   hipStream_t st = (hipStream_t)stream;
   if (rows == 0) return LVQ_OK;
   if (cols == 0) return zero_output(y, (size_t)batch * rows, st);
   switch (batch) {
-    case 1: return launch_bpdq<1>(codes, coeffs, rows, cols, x, y, st);
-    case 2: return launch_bpdq<2>(codes, coeffs, rows, cols, x, y, st);
-    case 3: return launch_bpdq<3>(codes, coeffs, rows, cols, x, y, st);
-    default: return launch_bpdq<4>(codes, coeffs, rows, cols, x, y, st);
+    case 1: return launch_bpdq_batch<1>(codes, coeffs, rows, cols, x, y, st);
+    case 2: return launch_bpdq_batch<2>(codes, coeffs, rows, cols, x, y, st);
+    case 3: return launch_bpdq_batch<3>(codes, coeffs, rows, cols, x, y, st);
+    default: return launch_bpdq_batch<4>(codes, coeffs, rows, cols, x, y, st);
   }
 }
