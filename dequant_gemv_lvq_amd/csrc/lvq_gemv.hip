@@ -545,6 +545,66 @@ __device__ __forceinline__ void decode_item(const MatSet& ms, int nb, int tau, i
   asm volatile("" ::: "memory");
 }
 
+// R rows at the same columns in one item (LP3 only): each 16-byte x read is
+// used by all R rows, so the LDS reads of x per weight fall by R.  Each row
+// adds its pairs into its own accumulators in exactly the order of
+// decode_item, so its result is the same bits as with one row per item.
+template <int B, int BPL, int M, int R>
+__device__ __forceinline__ void decode_rows(const MatSet& ms, int nb, int tau, int nchunks,
+                                            int kpad, int rows, int grp, int chunk, int lane,
+                                            const ItemRegs<BPL, M> (&g)[R], const uint2* lut,
+                                            const uint32_t* xs, float (&acc)[R][B][3]) {
+  static_assert(M == kSingle || M == kNoWeights, "rows per item > 1: plain LP3 only");
+  asm volatile("" ::: "memory");
+  const int npair = kpad / 2;
+  lds_u32* xl = (lds_u32*)xs + (chunk * (kWave * BPL) + lane) * 12;
+#pragma unroll
+  for (int u = 0; u < BPL; ++u) {
+    uint2 l[R];
+#pragma unroll
+    for (int i = 0; i < R; ++i) l[i] = lut[g[i].c[u]];
+#pragma unroll
+    for (int wi = 0; wi < 3; ++wi) {
+      uint32_t d[R][4];
+#pragma unroll
+      for (int i = 0; i < R; ++i)
+#pragma unroll
+        for (int vi = 0; vi < 4; ++vi) d[i][vi] = leech_pair(g[i].w[u][wi], vi, l[i].x, l[i].y);
+#pragma unroll
+      for (int bb = 0; bb < B; ++bb) {
+        const u32x4_t xv = *(lds_u32x4*)(xl + bb * npair + u * (kWave * 12) + 4 * wi);
+#pragma unroll
+        for (int i = 0; i < R; ++i) {
+          float& a = acc[i][bb][wi];
+          a = dot2(d[i][0], xv.x, a);
+          a = dot2(d[i][1], xv.y, a);
+          a = dot2(d[i][2], xv.z, a);
+          a = dot2(d[i][3], xv.w, a);
+        }
+      }
+    }
+  }
+  if (chunk == nchunks - 1) {
+    const uint16_t* xh = (const uint16_t*)xs;
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+      const int gr = grp * R + i;  // a row past the last loaded zeros: not written
+      const float s = half_bits_to_float((uint16_t)g[i].scale) * 16777216.0f;
+#pragma unroll
+      for (int bb = 0; bb < B; ++bb) {
+        float part = (acc[i][bb][0] + acc[i][bb][1] + acc[i][bb][2]) * s;
+        if (lane < tau)
+          part += half_bits_to_float((uint16_t)g[i].tail) *
+                  half_bits_to_float(xh[bb * kpad + 24 * nb + lane]);
+        const float tot = wave_sum_lane63(part);
+        if (lane == kWave - 1 && gr < rows) ms.y[0][(size_t)bb * rows + gr] = tot;
+        acc[i][bb][0] = acc[i][bb][1] = acc[i][bb][2] = 0.f;
+      }
+    }
+  }
+  asm volatile("" ::: "memory");
+}
+
 // The class table staged as per-class byte LUTs (leech_lut); class 0 gets
 // 0x00 in byte 0 so that an all-zero code word reads as +0 (valid class-0
 // code words never select byte 0).
@@ -574,8 +634,9 @@ __device__ __forceinline__ uint2 stage_lut(int c, uint64_t entry) {
 // the rotating mode, whose prologue holds 16-value butterfly sets, LP2
 // above batch 1, whose class extraction needs the registers, and the one-hot
 // mode, which keeps a block's four masks and its steps live across 12 pairs.)
-constexpr int leech_min_waves(int B, int BPL, int M, int D) {
-  return M != kGain && M != kRot && M != kOneHot && M != kLp2x && !(M == kLp2 && B > 1) &&
+constexpr int leech_min_waves(int B, int BPL, int M, int D, int R = 1) {
+  return R > 1 ? 4
+         : M != kGain && M != kRot && M != kOneHot && M != kLp2x && !(M == kLp2 && B > 1) &&
                  B + (D * BPL + 1) / 2 <= 4
              ? 8
              : 1;
@@ -838,9 +899,9 @@ __device__ __forceinline__ void rotate_x_lds(uint16_t* xh, float* fb, const floa
   }
 }
 
-template <int B, int BPL, int M, int D>
+template <int B, int BPL, int M, int D, int R>
 __global__ void __launch_bounds__(kMaxWgThreads)
-__attribute__((amdgpu_waves_per_eu(leech_min_waves(B, BPL, M, D))))
+__attribute__((amdgpu_waves_per_eu(leech_min_waves(B, BPL, M, D, R))))
 leech_gemv_kernel(MatSet ms, int rows, int nb, int tau, int cols, int nchunks, int kpad,
                   const uint16_t* __restrict__ x) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
@@ -852,8 +913,10 @@ leech_gemv_kernel(MatSet ms, int rows, int nb, int tau, int cols, int nchunks, i
   const int wpb = nthr / kWave;
   const int wave = __builtin_amdgcn_readfirstlane(blockIdx.x * wpb + (tid >> 6));
   const int nwaves = gridDim.x * wpb;
-  // this wave's items: rows wave, wave + nwaves, ..., each with nchunks chunks
-  const int myrows = wave < rows ? (rows - 1 - wave) / nwaves + 1 : 0;
+  // this wave's items: row groups (R rows each) wave, wave + nwaves, ...,
+  // each with nchunks chunks
+  const int ngroups = R == 1 ? rows : (rows + R - 1) / R;
+  const int myrows = wave < ngroups ? (ngroups - 1 - wave) / nwaves + 1 : 0;
   const int items = myrows * nchunks;
   const int per = kpad >> 3;  // 16-byte chunks per batch row of the staged x
   const int nq = B * per;
@@ -925,17 +988,25 @@ leech_gemv_kernel(MatSet ms, int rows, int nb, int tau, int cols, int nchunks, i
   //    whose item lies past the wave's last is loaded from an empty range (no
   //    memory request, every value 0), so the load sequence has no branch and
   //    every later wait counts exactly.
-  ItemRegs<BPL, M> ring[D];
+  ItemRegs<BPL, M> ring[D][R];
   int rr[D], rc[D];
   LaneOff lo = {lane * 2, lane * 4 * words_of(M)};
   lds_u32* const xlane = (lds_u32*)xs + lane * 12;
+  // item (row group g, chunk c): rows g R .. g R + R - 1; a row past the last
+  // is loaded from an empty range like an item past the wave's last
+  auto load_group = [&](int s, int g, int c, bool valid) {
+#pragma unroll
+    for (int i = 0; i < R; ++i)
+      load_item<BPL, M>(ms, nb, tau, g * R + i, c, valid && (R == 1 || g * R + i < rows), lo,
+                        ring[s][i]);
+  };
   {
     int r = wave, c = 0;
 #pragma unroll
     for (int s = 0; s < D; ++s) {
       rr[s] = r;
       rc[s] = c;
-      load_item<BPL, M>(ms, nb, tau, r, c, s < items, lo, ring[s]);
+      load_group(s, r, c, s < items);
       if (++c == nchunks) { c = 0; r += nwaves; }
     }
   }
@@ -952,10 +1023,20 @@ leech_gemv_kernel(MatSet ms, int rows, int nb, int tau, int cols, int nchunks, i
       rotate_x_lds((uint16_t*)xs + (size_t)bb * kpad, fb, qs, sw, ms, cols, tid, nthr);
   }
 
-  float acc[B][3];
+  float acc[R][B][3];
 #pragma unroll
-  for (int bb = 0; bb < B; ++bb) acc[bb][0] = acc[bb][1] = acc[bb][2] = 0.f;
+  for (int i = 0; i < R; ++i)
+#pragma unroll
+    for (int bb = 0; bb < B; ++bb) acc[i][bb][0] = acc[i][bb][1] = acc[i][bb][2] = 0.f;
   if (items == 0) return;
+  auto decode = [&](int s) {
+    if constexpr (R == 1)
+      decode_item<B, BPL, M>(ms, nb, tau, nchunks, kpad, rr[s], rc[s], lane, ring[s][0], lut, xs,
+                             xlane, acc[0]);
+    else
+      decode_rows<B, BPL, M, R>(ms, nb, tau, nchunks, kpad, rows, rr[s], rc[s], lane, ring[s],
+                                lut, xs, acc);
+  };
   // steady state: set s holds item j + s; decode it, then load item j + s + D
   // into the same registers, so D - 1 items stay in flight behind each decode
   auto advance = [&](int& r, int& c) {
@@ -966,18 +1047,15 @@ leech_gemv_kernel(MatSet ms, int rows, int nb, int tau, int cols, int nchunks, i
   for (; j + D < items; j += D) {
 #pragma unroll
     for (int s = 0; s < D; ++s) {
-      decode_item<B, BPL, M>(ms, nb, tau, nchunks, kpad, rr[s], rc[s], lane, ring[s], lut, xs,
-                             xlane, acc);
+      decode(s);
       advance(rr[s], rc[s]);
-      load_item<BPL, M>(ms, nb, tau, rr[s], rc[s], j + s + D < items, lo, ring[s]);
+      load_group(s, rr[s], rc[s], j + s + D < items);
     }
   }
   // the last one to D items, in sets 0 .. items - j - 1
 #pragma unroll
   for (int s = 0; s < D; ++s)
-    if (j + s < items)
-      decode_item<B, BPL, M>(ms, nb, tau, nchunks, kpad, rr[s], rc[s], lane, ring[s], lut, xs,
-                             xlane, acc);
+    if (j + s < items) decode(s);
 }
 
 // Rows shorter than one block: y = sum of the unquantized tail only.
@@ -1071,7 +1149,7 @@ typedef int OccupancyCache[kMaxDevices][3][2];
 // When set (lvq_gemv_launch_info), the Leech launch path records the launch
 // it would make here instead of making it.
 struct LaunchInfo {
-  int threads, workgroups, blocks_per_lane, ring, lds_bytes;
+  int threads, workgroups, blocks_per_lane, ring, lds_bytes, rows_per_item;
 };
 thread_local LaunchInfo* t_dry_run = nullptr;
 template <typename K>
@@ -1090,7 +1168,7 @@ int wgs_per_cu(OccupancyCache& cache, K kernel, int threads, size_t lds) {
   return n;
 }
 
-template <int B, int BPL, int M, int D>
+template <int B, int BPL, int M, int D, int R = 1>
 int launch_leech_mode(const MatSet& ms, int rows, int cols, const uint16_t* x, hipStream_t st) {
   const int nb = cols / 24, tau = cols % 24;
   const int nchunks = (nb + kWave * BPL - 1) / (kWave * BPL);
@@ -1105,27 +1183,44 @@ int launch_leech_mode(const MatSet& ms, int rows, int cols, const uint16_t* x, h
   }
   if (lds > device_lds_bytes()) return LVQ_E_SHAPE;
   const int cus = device_cus();
-  const int threads = wg_threads(rows, cus);
+  const int groups = (rows + R - 1) / R;  // items hold R rows each
+  const int threads = R > 1 ? 512 : wg_threads(groups, cus);
   const int wpb = threads / kWave;
   // as many workgroups as fit on the chip at once (one or two per CU, by
-  // registers and LDS), rows grid-strided over their waves
+  // registers and LDS), row groups grid-strided over their waves
   static OccupancyCache occupancy;  // this instantiation's own
-  const int occ = wgs_per_cu(occupancy, leech_gemv_kernel<B, BPL, M, D>, threads, lds);
-  long long wgs = ((long long)rows + wpb - 1) / wpb;
+  const int occ = wgs_per_cu(occupancy, leech_gemv_kernel<B, BPL, M, D, R>, threads, lds);
+  long long wgs = ((long long)groups + wpb - 1) / wpb;
   if (wgs > (long long)occ * cus) wgs = (long long)occ * cus;
   if (wgs < 1) wgs = 1;
   if (t_dry_run) {
-    *t_dry_run = {threads, (int)wgs, BPL, D, (int)lds};
+    *t_dry_run = {threads, (int)wgs, BPL, D, (int)lds, R};
     return LVQ_OK;
   }
   clear_hip_error();
-  hipLaunchKernelGGL((leech_gemv_kernel<B, BPL, M, D>), dim3((unsigned)wgs), dim3(threads), lds,
+  hipLaunchKernelGGL((leech_gemv_kernel<B, BPL, M, D, R>), dim3((unsigned)wgs), dim3(threads), lds,
                      st, ms, rows, nb, tau, cols, nchunks, (int)kpad, x);
   return launch_status();
 }
 
+// Rows per item.  At batch 3 and 4, with enough rows that pairs of rows
+// still give every SIMD four waves of 512-thread workgroups, an item holds
+// two rows at the same columns (each x read from LDS serves both) and a CU
+// runs two workgroups whose staging and decode phases overlap: 12288 x 4096
+// at batch 4 14.5 -> 13.2 us, at batch 3 12.1 -> 11.5.  At batch 2 the x
+// reads saved do not pay for the lost waves (9.6 -> 10.1 us), and with fewer
+// rows the pairs leave too few waves to hide the loads (4096 x 12288 at batch
+// 4: 12.7 -> 13.4 us); three rows per item lose everywhere.
+inline int rows_per_item(int B, int mode, int nb, int rows, int cus) {
+  return B >= 3 && (mode == kSingle || mode == kNoWeights) && (long long)rows >= 32LL * cus ? 2 : 1;
+}
+
 template <int B, int BPL, int M>
 int launch_leech_ring(const MatSet& ms, int rows, int cols, const uint16_t* x, hipStream_t st) {
+  if constexpr (B >= 3 && BPL == 1 && (M == kSingle || M == kNoWeights)) {
+    if (rows_per_item(B, M, cols / 24, rows, device_cus()) == 2)
+      return launch_leech_mode<B, BPL, M, 2, 2>(ms, rows, cols, x, st);
+  }
   if constexpr (BPL == 1 && M != kFused && M != kRot) {
     if (short_rows(M, cols / 24, rows)) return launch_leech_mode<B, BPL, M, 3>(ms, rows, cols, x, st);
   }
@@ -1376,7 +1471,7 @@ extern "C" int lvq_gemv_launch_info(int kind, int rows, int cols, int batch, int
   if (rows < 1 || cols < 24) return LVQ_E_SHAPE;
   static const int modes[] = {kSingle, kRot, kDirect, kOneHot, kLp2, kGain, kNoWeights};
   if (kind < 0 || kind >= (int)(sizeof(modes) / sizeof(modes[0]))) return LVQ_E_SHAPE;
-  LaunchInfo info = {0, 0, 0, 0, 0};
+  LaunchInfo info = {0, 0, 0, 0, 0, 0};
   t_dry_run = &info;
   const uintptr_t fake = (uintptr_t)1 << 30;
   const void* blob = (const void*)fake;
@@ -1396,5 +1491,6 @@ extern "C" int lvq_gemv_launch_info(int kind, int rows, int cols, int batch, int
   info_out[2] = info.blocks_per_lane;
   info_out[3] = info.ring;
   info_out[4] = info.lds_bytes;
+  info_out[5] = info.rows_per_item;
   return LVQ_OK;
 }
