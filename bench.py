@@ -1015,13 +1015,14 @@ def profile_only(torch, lvq, args):
         yd = torch.empty((1, ROWS), dtype=torch.float32, device="cuda")
         fn = lambda i: lvq.fp16_gemv(bufs[i % n], ROWS, COLS, xd, yd, 1)  # noqa: E731
     elif args.profile == "bpdq":
+        bt = args.profile_batch
         d = synth.bpdq_matrix(4096, 4096)
         n = copies_for(bpdq_bytes(4096, 4096))
         codes = dev_copies(torch, d["codes"], n)
         coeffs = dev_copies(torch, d["coeffs"], n)
-        xd = to_dev(torch, synth.activations(4096, 1, 2, rows=4096))
-        yd = torch.empty((1, 4096), dtype=torch.float32, device="cuda")
-        fn = lambda i: lvq.bpdq_gemv(codes[i % n], coeffs[i % n], 4096, 4096, xd, yd, 1)  # noqa
+        xd = to_dev(torch, synth.activations(4096, bt, 2, rows=4096))
+        yd = torch.empty((bt, 4096), dtype=torch.float32, device="cuda")
+        fn = lambda i: lvq.bpdq_gemv(codes[i % n], coeffs[i % n], 4096, 4096, xd, yd, bt)  # noqa
     else:
         d = synth.trellis_matrix(ROWS, COLS)
         n = copies_for(trellis_bytes(ROWS, COLS))
