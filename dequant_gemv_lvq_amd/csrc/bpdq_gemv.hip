@@ -9,36 +9,37 @@
 // plane i selects, and a deterministic split over K.
 //
 // gfx950 design.  The layout puts consecutive rows in consecutive words, so a
-// lane is a (row, unit) pair, a unit being U consecutive code words (16 U
-// columns, a quarter or a half of a group): a workgroup covers 16 rows x
-// SLOTS units, every load instruction of a wave reads four 64-byte runs (16
-// rows of 4 units), and a lane walks its units SLOTS apart, the next unit's
-// words requested while the current one is summed.  The form is linear, so
-// each lane applies its group's coefficients to its own unit:
-// c0 * S0u + c1 * S1u + c2 * Xu, with Xu the sum of x over the unit.  Bits
-// are never shifted into place: a mask keeps bit 2c (plane 0) or 2c+1 (plane
-// 1) of the columns c and c+8 of a word, and that masked word, read as two
-// fp16 subnormals (2^(2c) or 2^(2c+1) times 2^-24), goes straight into
-// v_dot2_f32_f16 against the x pair (x_c, x_{c+8}); columns 5..7 use the word
-// shifted right by 10.  Ten fp32 accumulators per batch row (2 planes x 5
-// powers of two) are rescaled exactly at the end of each unit.  x pairs and
-// unit sums are staged in LDS once per workgroup, the x words requested
-// before the code words so the copy runs under their latency; the SLOTS
-// partials of a row are summed by shuffles inside a wave and then over the
-// waves in LDS, always in the same order.  Neighbouring 16-row tiles share
-// 128-byte lines and are mapped to workgroups on the same XCD.
+// lane is a (row, quarter group) pair, a quarter being 4 consecutive code
+// words (64 columns): a workgroup covers 16 rows x SLOTS quarters, every load
+// instruction of a wave reads four 64-byte runs (16 rows of 4 quarters), and
+// a lane walks its quarters SLOTS apart, the next quarter's words requested
+// while the current one is summed.  The form is linear, so each lane applies
+// its group's coefficients to its own quarter: c0 * S0q + c1 * S1q + c2 * Xq,
+// with Xq the sum of x over the quarter.  Bits are never shifted into place:
+// a mask keeps bit 2c (plane 0) or 2c+1 (plane 1) of the columns c and c+8
+// of a word, and that masked word, read as two fp16 subnormals (2^(2c) or
+// 2^(2c+1) times 2^-24), goes straight into v_dot2_f32_f16 against the x
+// pair (x_c, x_{c+8}); columns 5..7 use the word shifted right by 10.  Ten
+// fp32 accumulators per batch row (2 planes x 5 powers of two) are rescaled
+// exactly at the end of each quarter.  x pairs and quarter sums are staged in
+// LDS once per workgroup, the x words requested before the code words so the
+// copy runs under their latency; the SLOTS partials of a row are summed by
+// shuffles inside a wave and then over the waves in LDS, always in the same
+// order.  Neighbouring 16-row tiles share 128-byte lines and are mapped to
+// workgroups on the same XCD.
 
 #include "common.h"
 
 namespace lvq {
 
 constexpr int kBpdqRows = 16;
+constexpr int kBpdqUnit = 4;  // code words per lane unit: a quarter group
 
-template <int B, int U, int SLOTS>
+template <int B, int SLOTS>
 __global__ void __launch_bounds__(kBpdqRows * SLOTS)
 bpdq_gemv_kernel(const uint32_t* __restrict__ codes, const uint16_t* __restrict__ coeffs,
                  int rows, int cols, const uint16_t* __restrict__ x, float* __restrict__ y) {
-  static_assert(U == 4 || U == 8 || U == 16, "a unit is a quarter, half or whole group");
+  constexpr int U = kBpdqUnit;
   constexpr int kThreads = kBpdqRows * SLOTS, kWaves = kThreads / kWave;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const int nwords = cols / 16, nunits = nwords / U;
@@ -97,10 +98,10 @@ bpdq_gemv_kernel(const uint32_t* __restrict__ codes, const uint16_t* __restrict_
   load_unit(slot);
 
   // 3. x pairs (x_c, x_{c+8}) of each code word, and the sum of x over each
-  //    unit, into LDS.  The thread that pairs a word also sums its 16 values
-  //    (v_dot2 against (1, 1), fixed order); the U words of a unit sit in U
-  //    neighbouring lanes of one DPP row and are added by quad swaps and
-  //    mirrors, the same operands on every lane.
+  //    quarter, into LDS.  The thread that pairs a word also sums its 16
+  //    values (v_dot2 against (1, 1), fixed order); the 4 words of a quarter
+  //    sit in the 4 lanes of a quad and are added by two quad swaps, the same
+  //    operands on every lane.
   auto stage = [&](int i, uint4 lo, uint4 hi) {
     const uint32_t a[4] = {lo.x, lo.y, lo.z, lo.w}, b[4] = {hi.x, hi.y, hi.z, hi.w};
     uint32_t p[8];
@@ -114,14 +115,12 @@ bpdq_gemv_kernel(const uint32_t* __restrict__ codes, const uint16_t* __restrict_
                dot2(a[3], kOnes, dot2(a[2], kOnes, 0.f))) +
               (dot2(b[1], kOnes, dot2(b[0], kOnes, 0.f)) +
                dot2(b[3], kOnes, dot2(b[2], kOnes, 0.f)));
-    s = dpp_add<0x4E, 0xF>(dpp_add<0xB1, 0xF>(s));  // quad_perm swaps: 4 words
-    if (U >= 8) s = dpp_add<0x141, 0xF>(s);          // row_half_mirror: 8 words
-    if (U >= 16) s = dpp_add<0x140, 0xF>(s);         // row_mirror: 16 words
+    s = dpp_add<0x4E, 0xF>(dpp_add<0xB1, 0xF>(s));  // quad_perm swaps: the quarter's 4 words
     if (i < nst) {
       uint4* d = (uint4*)(xp + (size_t)i * 8);
       d[0] = make_uint4(p[0], p[1], p[2], p[3]);
       d[1] = make_uint4(p[4], p[5], p[6], p[7]);
-      if (i % U == 0) xu[i / U] = s;  // word i of batch row bb: unit bb * nunits + w / U
+      if (i % U == 0) xu[i / U] = s;  // word i of batch row bb: quarter bb * nunits + w / 4
     }
   };
 #pragma unroll
@@ -210,53 +209,34 @@ bpdq_gemv_kernel(const uint32_t* __restrict__ codes, const uint16_t* __restrict_
 
 int zero_output(float* y, size_t n, hipStream_t st);
 
-template <int B, int U, int SLOTS>
+template <int B, int SLOTS>
 int launch_bpdq(const uint32_t* codes, const uint16_t* coeffs, int rows, int cols,
                 const uint16_t* x, float* y, hipStream_t st) {
   constexpr int kThreads = kBpdqRows * SLOTS;
-  const size_t lds = (size_t)B * cols * 2 + (size_t)B * (cols / (16 * U)) * 4 +
+  const size_t lds = (size_t)B * cols * 2 + (size_t)B * (cols / (16 * kBpdqUnit)) * 4 +
                      (size_t)(kThreads / kWave) * kBpdqRows * B * 4;
   if (lds > device_lds_bytes()) return LVQ_E_SHAPE;
   const int ntiles = (rows + kBpdqRows - 1) / kBpdqRows;
   clear_hip_error();
-  hipLaunchKernelGGL((bpdq_gemv_kernel<B, U, SLOTS>), dim3(ntiles), dim3(kThreads), lds, st,
-                     codes, coeffs, rows, cols, x, y);
+  hipLaunchKernelGGL((bpdq_gemv_kernel<B, SLOTS>), dim3(ntiles), dim3(kThreads), lds, st, codes,
+                     coeffs, rows, cols, x, y);
   return launch_status();
 }
 
-// Lane shapes (unit words, slots), most slots first.  Each lane takes about
-// two units, the next unit's words requested while the current one is summed:
-// the fewest units per lane that is at least two, else the most; ties go to
-// more slots (more waves).  At 4096 x 4096 that is quarters, 32 slots (two
-// waves per SIMD); at 4096 x 12288 quarters, 64 slots, three per lane.
-struct BpdqShape {
-  int unit, slots;
-};
-constexpr BpdqShape kBpdqShapes[] = {{4, 64}, {8, 32}, {4, 32}, {8, 16}};
-constexpr int kNumBpdqShapes = sizeof(kBpdqShapes) / sizeof(kBpdqShapes[0]);
-
-inline int bpdq_shape(int cols) {
-  int best = -1, bk = 0;
-  for (int i = 0; i < kNumBpdqShapes; ++i) {
-    const int nunits = cols / 16 / kBpdqShapes[i].unit;
-    const int k = (nunits + kBpdqShapes[i].slots - 1) / kBpdqShapes[i].slots;
-    if (best < 0 || (k >= 2 ? (bk < 2 || k < bk) : (bk < 2 && k > bk))) {
-      best = i;
-      bk = k;
-    }
-  }
-  return best;
-}
-
+// Quarters per workgroup row: each lane should take about two quarters (the
+// next one's words requested while the current one is summed), so the most
+// slots of 64, 32 and 16 that still give two per lane, else 16.  At 4096
+// columns 32 slots (512-thread workgroups, two waves per SIMD), at 12288 64
+// slots and three quarters per lane.  Measured over the six shapes of a
+// Qwen3-8B layer against whole or half groups per lane and other slot counts:
+// within 0.14 us of the best at batch 1 and 0.6 us at batch 4.
 template <int B>
 int launch_bpdq_batch(const uint32_t* codes, const uint16_t* coeffs, int rows, int cols,
                       const uint16_t* x, float* y, hipStream_t st) {
-  switch (bpdq_shape(cols)) {
-    case 0: return launch_bpdq<B, 4, 64>(codes, coeffs, rows, cols, x, y, st);
-    case 1: return launch_bpdq<B, 8, 32>(codes, coeffs, rows, cols, x, y, st);
-    case 2: return launch_bpdq<B, 4, 32>(codes, coeffs, rows, cols, x, y, st);
-    default: return launch_bpdq<B, 8, 16>(codes, coeffs, rows, cols, x, y, st);
-  }
+  const int quarters = cols / 64;
+  if (quarters >= 2 * 64) return launch_bpdq<B, 64>(codes, coeffs, rows, cols, x, y, st);
+  if (quarters >= 2 * 32) return launch_bpdq<B, 32>(codes, coeffs, rows, cols, x, y, st);
+  return launch_bpdq<B, 16>(codes, coeffs, rows, cols, x, y, st);
 }
 
 }  // namespace lvq

@@ -171,7 +171,9 @@ def test_fp16_gemv(rows, cols, batch):
 # ---------------------------------------------------------------- BPDQ
 
 @pytest.mark.parametrize("rows,cols,batch", [(4096, 4096, 1), (4096, 4096, 4), (33, 256, 1),
-                                             (100, 4352, 2)])
+                                             (100, 4352, 2), (300, 1024, 3),
+                                             # 64 quarters per workgroup row
+                                             (4096, 12288, 1), (12288, 4096, 4)])
 def test_bpdq_gemv(rows, cols, batch):
     d = synth.bpdq_matrix(rows, cols)
     x = synth.activations(cols, batch, 2, rows=rows)
