@@ -405,10 +405,9 @@ LAUNCH_KINDS = {"gemv": 0, "rotated": 1, "direct": 2, "onehot": 3, "lp2": 4, "ga
 
 def gemv_launch_info(kind: str, rows: int, cols: int, batch: int = 1, m: int = 1) -> dict:
     """The launch a Leech GEMV entry point makes for this shape (nothing is
-    launched): threads, workgroups, blocks per lane, ring depth, LDS bytes,
-    rows per item."""
-    out = (ctypes.c_int * 6)()
+    launched): threads, workgroups, blocks per lane, ring depth, LDS bytes."""
+    out = (ctypes.c_int * 5)()
     _check(_lib.lvq_gemv_launch_info(LAUNCH_KINDS[kind], int(rows), int(cols), int(batch),
                                      int(m), out))
     return {"threads": out[0], "workgroups": out[1], "blocks_per_lane": out[2],
-            "ring": out[3], "lds_bytes": out[4], "rows_per_item": out[5]}
+            "ring": out[3], "lds_bytes": out[4]}

@@ -383,12 +383,24 @@ __device__ __forceinline__ void load_item(const MatSet& ms, int nb, int tau, int
   load_codes<BPL, M>(ms, nb, gr, chunk, valid, lo, g);
 }
 
-// LDS layout (dynamic): lut uint2[302] | x fp16 [B][kpad], kpad >= 24 * npad and
-// >= cols, a multiple of 512, with npad = nchunks * 64 * BPL blocks; columns past
-// cols are zero (the rotating mode adds its f32 buffer, Q and sign words after
-// x).  The 32-bit pair feeding view v of code word w of block k is element
-// 12k + 4w + v of a batch row (natural column order; in the direct and
-// one-hot layouts pair P = 3w + v, element 12k + P).
+// LDS layout (dynamic): lut uint2[302] | x.  At batch 1, and in the rotating
+// mode, x is fp16 [B][kpad], kpad >= 24 * npad and >= cols, a multiple of 512,
+// with npad = nchunks * 64 * BPL blocks; columns past cols are zero (the
+// rotating mode adds its f32 buffer, Q and sign words after x).  The 32-bit
+// pair feeding view v of code word w of block k is element 12k + 4w + v of a
+// batch row (natural column order; in the direct and one-hot layouts pair
+// P = 3w + v, element 12k + P).
+// Above batch 1 (other modes) x is chunk-major: the 64 BPL 24 columns of
+// chunk c of batch row bb at (c B + bb) 64 BPL 24 halves, then the tail
+// columns 24 nb .. 24 nb + 23 of every batch row, 32 halves each.  The batch
+// stride is then a constant of the kernel, so every x read of an item takes
+// an immediate offset from one per-item base (with the run-time stride
+// kpad each read of batch rows 1.. paid an address add).
+template <int B, int M>
+constexpr bool x_chunk_major() { return B >= 2 && M != kRot; }
+template <int BPL>
+constexpr int x_chunk_dwords() { return kWave * BPL * 12; }  // one chunk of one batch row
+
 template <int B, int BPL, int M>
 __device__ __forceinline__ void decode_item(const MatSet& ms, int nb, int tau, int nchunks,
                                             int kpad, int gr, int chunk, int lane,
@@ -401,13 +413,16 @@ __device__ __forceinline__ void decode_item(const MatSet& ms, int nb, int tau, i
   // into the same registers whatever the blocks-per-lane of the launch, so a
   // row's result does not depend on the launch geometry (or on which other
   // matrices share the launch).
-  const int npair = kpad / 2;
+  constexpr bool kXC = x_chunk_major<B, M>();
+  constexpr int kXS = x_chunk_dwords<BPL>();
+  const int npair = kXC ? kXS : kpad / 2;  // batch-row stride of x, 32-bit words
   // The 16 bytes of x at 32-bit word o of the lane's x (word 0 = the pair
   // feeding view 0 of code word 0 of this item's first block, batch row 0),
   // through a 32-bit LDS pointer.  Batch 1 starts from this lane's base, set
   // once per kernel (one add per item); above batch 1 that extra live register
   // pushes the 64-VGPR variants into spills, so the address is formed per item.
   lds_u32* xl = B == 1 ? xlane + chunk * (kWave * BPL * 12)
+                : kXC  ? (lds_u32*)xs + chunk * (B * kXS) + lane * 12
                        : (lds_u32*)xs + (chunk * (kWave * BPL) + lane) * 12;
   auto xq = [&](int o) -> u32x4_t { return *(lds_u32x4*)(xl + o); };
 #pragma unroll
@@ -504,10 +519,11 @@ __device__ __forceinline__ void decode_item(const MatSet& ms, int nb, int tau, i
       const uint32_t e0 = __builtin_amdgcn_readfirstlane(g.e0);
       const uint32_t e1 = __builtin_amdgcn_readfirstlane(g.e1);
       if (e0 != e1) {
-        const int npair = kpad / 2;
         for (uint32_t e = e0 + lane; e < e1; e += kWave) {
           const uint4 ent = ms.exc[e];
           const int k = (int)(ent.x & 0xFFFFu);
+          // batch row 0's pairs of block k
+          const int xk = kXC ? (k / (kWave * BPL)) * (B * kXS) + (k % (kWave * BPL)) * 12 : 12 * k;
           const uint2 l = leech_lut(ms.v[0].table[ent.x >> 16]);  // never class 0
           const uint32_t w[3] = {ent.y, ent.z, ent.w};
 #pragma unroll
@@ -517,7 +533,7 @@ __device__ __forceinline__ void decode_item(const MatSet& ms, int nb, int tau, i
               const uint32_t d = leech_pair(w[wi], vi, l.x, l.y);
 #pragma unroll
               for (int bb = 0; bb < B; ++bb)
-                acc[bb][wi] = dot2(d, xs[bb * npair + 12 * k + 4 * wi + vi], acc[bb][wi]);
+                acc[bb][wi] = dot2(d, xs[bb * npair + xk + 4 * wi + vi], acc[bb][wi]);
             }
           }
         }
@@ -531,7 +547,8 @@ __device__ __forceinline__ void decode_item(const MatSet& ms, int nb, int tau, i
       float part = (acc[bb][0] + acc[bb][1] + acc[bb][2]) * s;
       if (lane < tau)
         part += half_bits_to_float((uint16_t)g.tail) *
-                half_bits_to_float(xh[bb * kpad + 24 * nb + lane]);
+                half_bits_to_float(kXC ? xh[nchunks * B * 2 * kXS + bb * 32 + lane]
+                                       : xh[bb * kpad + 24 * nb + lane]);
       const float tot = wave_sum_lane63(part);
       if (lane == kWave - 1) {
         const int m = mat_of<M>(ms, gr);
@@ -540,66 +557,6 @@ __device__ __forceinline__ void decode_item(const MatSet& ms, int nb, int tau, i
         pick<M>(ms, m, [](const MatSet& s, int i) { return s.y[i]; })[(size_t)bb * rows_m + (gr - s0)] = tot;
       }
       acc[bb][0] = acc[bb][1] = acc[bb][2] = 0.f;
-    }
-  }
-  asm volatile("" ::: "memory");
-}
-
-// R rows at the same columns in one item (LP3 only): each 16-byte x read is
-// used by all R rows, so the LDS reads of x per weight fall by R.  Each row
-// adds its pairs into its own accumulators in exactly the order of
-// decode_item, so its result is the same bits as with one row per item.
-template <int B, int BPL, int M, int R>
-__device__ __forceinline__ void decode_rows(const MatSet& ms, int nb, int tau, int nchunks,
-                                            int kpad, int rows, int grp, int chunk, int lane,
-                                            const ItemRegs<BPL, M> (&g)[R], const uint2* lut,
-                                            const uint32_t* xs, float (&acc)[R][B][3]) {
-  static_assert(M == kSingle || M == kNoWeights, "rows per item > 1: plain LP3 only");
-  asm volatile("" ::: "memory");
-  const int npair = kpad / 2;
-  lds_u32* xl = (lds_u32*)xs + (chunk * (kWave * BPL) + lane) * 12;
-#pragma unroll
-  for (int u = 0; u < BPL; ++u) {
-    uint2 l[R];
-#pragma unroll
-    for (int i = 0; i < R; ++i) l[i] = lut[g[i].c[u]];
-#pragma unroll
-    for (int wi = 0; wi < 3; ++wi) {
-      uint32_t d[R][4];
-#pragma unroll
-      for (int i = 0; i < R; ++i)
-#pragma unroll
-        for (int vi = 0; vi < 4; ++vi) d[i][vi] = leech_pair(g[i].w[u][wi], vi, l[i].x, l[i].y);
-#pragma unroll
-      for (int bb = 0; bb < B; ++bb) {
-        const u32x4_t xv = *(lds_u32x4*)(xl + bb * npair + u * (kWave * 12) + 4 * wi);
-#pragma unroll
-        for (int i = 0; i < R; ++i) {
-          float& a = acc[i][bb][wi];
-          a = dot2(d[i][0], xv.x, a);
-          a = dot2(d[i][1], xv.y, a);
-          a = dot2(d[i][2], xv.z, a);
-          a = dot2(d[i][3], xv.w, a);
-        }
-      }
-    }
-  }
-  if (chunk == nchunks - 1) {
-    const uint16_t* xh = (const uint16_t*)xs;
-#pragma unroll
-    for (int i = 0; i < R; ++i) {
-      const int gr = grp * R + i;  // a row past the last loaded zeros: not written
-      const float s = half_bits_to_float((uint16_t)g[i].scale) * 16777216.0f;
-#pragma unroll
-      for (int bb = 0; bb < B; ++bb) {
-        float part = (acc[i][bb][0] + acc[i][bb][1] + acc[i][bb][2]) * s;
-        if (lane < tau)
-          part += half_bits_to_float((uint16_t)g[i].tail) *
-                  half_bits_to_float(xh[bb * kpad + 24 * nb + lane]);
-        const float tot = wave_sum_lane63(part);
-        if (lane == kWave - 1 && gr < rows) ms.y[0][(size_t)bb * rows + gr] = tot;
-        acc[i][bb][0] = acc[i][bb][1] = acc[i][bb][2] = 0.f;
-      }
     }
   }
   asm volatile("" ::: "memory");
@@ -634,9 +591,8 @@ __device__ __forceinline__ uint2 stage_lut(int c, uint64_t entry) {
 // the rotating mode, whose prologue holds 16-value butterfly sets, LP2
 // above batch 1, whose class extraction needs the registers, and the one-hot
 // mode, which keeps a block's four masks and its steps live across 12 pairs.)
-constexpr int leech_min_waves(int B, int BPL, int M, int D, int R = 1) {
-  return R > 1 ? 4
-         : M != kGain && M != kRot && M != kOneHot && M != kLp2x && !(M == kLp2 && B > 1) &&
+constexpr int leech_min_waves(int B, int BPL, int M, int D) {
+  return M != kGain && M != kRot && M != kOneHot && M != kLp2x && !(M == kLp2 && B > 1) &&
                  B + (D * BPL + 1) / 2 <= 4
              ? 8
              : 1;
@@ -899,9 +855,9 @@ __device__ __forceinline__ void rotate_x_lds(uint16_t* xh, float* fb, const floa
   }
 }
 
-template <int B, int BPL, int M, int D, int R>
+template <int B, int BPL, int M, int D>
 __global__ void __launch_bounds__(kMaxWgThreads)
-__attribute__((amdgpu_waves_per_eu(leech_min_waves(B, BPL, M, D, R))))
+__attribute__((amdgpu_waves_per_eu(leech_min_waves(B, BPL, M, D))))
 leech_gemv_kernel(MatSet ms, int rows, int nb, int tau, int cols, int nchunks, int kpad,
                   const uint16_t* __restrict__ x) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
@@ -913,10 +869,8 @@ leech_gemv_kernel(MatSet ms, int rows, int nb, int tau, int cols, int nchunks, i
   const int wpb = nthr / kWave;
   const int wave = __builtin_amdgcn_readfirstlane(blockIdx.x * wpb + (tid >> 6));
   const int nwaves = gridDim.x * wpb;
-  // this wave's items: row groups (R rows each) wave, wave + nwaves, ...,
-  // each with nchunks chunks
-  const int ngroups = R == 1 ? rows : (rows + R - 1) / R;
-  const int myrows = wave < ngroups ? (ngroups - 1 - wave) / nwaves + 1 : 0;
+  // this wave's items: rows wave, wave + nwaves, ..., each with nchunks chunks
+  const int myrows = wave < rows ? (rows - 1 - wave) / nwaves + 1 : 0;
   const int items = myrows * nchunks;
   const int per = kpad >> 3;  // 16-byte chunks per batch row of the staged x
   const int nq = B * per;
@@ -932,7 +886,36 @@ leech_gemv_kernel(MatSet ms, int rows, int nb, int tau, int cols, int nchunks, i
   //    late wave's copies queued behind other waves' weight loads (measured:
   //    7.70 -> 7.45 us at 4096 x 12288, batch 1).  Larger copies go to every
   //    wave (issuing 24+ copies per wave costs more than it saves).
-  if (vec) {
+  //    Chunk-major x (above batch 1): 1 KiB unit q of the region goes to
+  //    byte q * 1024, from column c 64 BPL 24 + 512 k of its batch row (3 BPL
+  //    units per chunk and batch row); then the tail columns, one per thread.
+  constexpr bool kXC = x_chunk_major<B, M>();
+  if (kXC) {
+    constexpr int kU = 3 * BPL, kXW = 2 * x_chunk_dwords<BPL>();  // units, halves per chunk row
+    uint16_t* xh = (uint16_t*)xs;
+    const int nu = nchunks * B * kU;
+    if (vec) {
+      const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+      const int nx = nu > 32 || wpb < 4 ? wpb : 4;
+      for (int q = wv < nx ? wv : nu; q < nu; q += nx) {
+        const int cb = q / kU, k = q - cb * kU, c = cb / B, bb = cb - c * B;
+        const auto rx = buffer_rsrc(x + (size_t)bb * cols, (uint32_t)cols * 2);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rx, (__attribute__((address_space(3))) void*)((uint8_t*)xs + (size_t)q * 1024), 16,
+            lane * 16, c * (kXW * 2) + k * 1024, 0, 0);
+      }
+    } else {
+      for (int i = tid; i < nchunks * B * kXW; i += nthr) {
+        const int cb = i / kXW, e = i - cb * kXW, c = cb / B, bb = cb - c * B;
+        const int col = c * kXW + e;
+        xh[i] = col < cols ? x[(size_t)bb * cols + col] : (uint16_t)0;
+      }
+    }
+    for (int i = tid; i < B * 32; i += nthr) {
+      const int bb = i >> 5, t = i & 31;
+      xh[nchunks * B * kXW + i] = t < tau ? x[(size_t)bb * cols + 24 * nb + t] : (uint16_t)0;
+    }
+  } else if (vec) {
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int nx = nq > 32 * kWave || wpb < 4 ? wpb : 4;
     for (int q = wv < nx ? wv : nq; q * kWave < nq; q += nx) {
@@ -988,25 +971,17 @@ leech_gemv_kernel(MatSet ms, int rows, int nb, int tau, int cols, int nchunks, i
   //    whose item lies past the wave's last is loaded from an empty range (no
   //    memory request, every value 0), so the load sequence has no branch and
   //    every later wait counts exactly.
-  ItemRegs<BPL, M> ring[D][R];
+  ItemRegs<BPL, M> ring[D];
   int rr[D], rc[D];
   LaneOff lo = {lane * 2, lane * 4 * words_of(M)};
   lds_u32* const xlane = (lds_u32*)xs + lane * 12;
-  // item (row group g, chunk c): rows g R .. g R + R - 1; a row past the last
-  // is loaded from an empty range like an item past the wave's last
-  auto load_group = [&](int s, int g, int c, bool valid) {
-#pragma unroll
-    for (int i = 0; i < R; ++i)
-      load_item<BPL, M>(ms, nb, tau, g * R + i, c, valid && (R == 1 || g * R + i < rows), lo,
-                        ring[s][i]);
-  };
   {
     int r = wave, c = 0;
 #pragma unroll
     for (int s = 0; s < D; ++s) {
       rr[s] = r;
       rc[s] = c;
-      load_group(s, r, c, s < items);
+      load_item<BPL, M>(ms, nb, tau, r, c, s < items, lo, ring[s]);
       if (++c == nchunks) { c = 0; r += nwaves; }
     }
   }
@@ -1023,19 +998,13 @@ leech_gemv_kernel(MatSet ms, int rows, int nb, int tau, int cols, int nchunks, i
       rotate_x_lds((uint16_t*)xs + (size_t)bb * kpad, fb, qs, sw, ms, cols, tid, nthr);
   }
 
-  float acc[R][B][3];
+  float acc[B][3];
 #pragma unroll
-  for (int i = 0; i < R; ++i)
-#pragma unroll
-    for (int bb = 0; bb < B; ++bb) acc[i][bb][0] = acc[i][bb][1] = acc[i][bb][2] = 0.f;
+  for (int bb = 0; bb < B; ++bb) acc[bb][0] = acc[bb][1] = acc[bb][2] = 0.f;
   if (items == 0) return;
   auto decode = [&](int s) {
-    if constexpr (R == 1)
-      decode_item<B, BPL, M>(ms, nb, tau, nchunks, kpad, rr[s], rc[s], lane, ring[s][0], lut, xs,
-                             xlane, acc[0]);
-    else
-      decode_rows<B, BPL, M, R>(ms, nb, tau, nchunks, kpad, rows, rr[s], rc[s], lane, ring[s],
-                                lut, xs, acc);
+    decode_item<B, BPL, M>(ms, nb, tau, nchunks, kpad, rr[s], rc[s], lane, ring[s], lut, xs, xlane,
+                           acc);
   };
   // steady state: set s holds item j + s; decode it, then load item j + s + D
   // into the same registers, so D - 1 items stay in flight behind each decode
@@ -1049,7 +1018,7 @@ leech_gemv_kernel(MatSet ms, int rows, int nb, int tau, int cols, int nchunks, i
     for (int s = 0; s < D; ++s) {
       decode(s);
       advance(rr[s], rc[s]);
-      load_group(s, rr[s], rc[s], j + s + D < items);
+      load_item<BPL, M>(ms, nb, tau, rr[s], rc[s], j + s + D < items, lo, ring[s]);
     }
   }
   // the last one to D items, in sets 0 .. items - j - 1
@@ -1149,7 +1118,7 @@ typedef int OccupancyCache[kMaxDevices][3][2];
 // When set (lvq_gemv_launch_info), the Leech launch path records the launch
 // it would make here instead of making it.
 struct LaunchInfo {
-  int threads, workgroups, blocks_per_lane, ring, lds_bytes, rows_per_item;
+  int threads, workgroups, blocks_per_lane, ring, lds_bytes;
 };
 thread_local LaunchInfo* t_dry_run = nullptr;
 template <typename K>
@@ -1168,14 +1137,15 @@ int wgs_per_cu(OccupancyCache& cache, K kernel, int threads, size_t lds) {
   return n;
 }
 
-template <int B, int BPL, int M, int D, int R = 1>
+template <int B, int BPL, int M, int D>
 int launch_leech_mode(const MatSet& ms, int rows, int cols, const uint16_t* x, hipStream_t st) {
   const int nb = cols / 24, tau = cols % 24;
   const int nchunks = (nb + kWave * BPL - 1) / (kWave * BPL);
   const size_t npad = (size_t)nchunks * kWave * BPL;
   size_t kpad = npad * 24 > (size_t)cols ? npad * 24 : (size_t)cols;
   kpad = (kpad + 511) & ~(size_t)511;
-  size_t lds = (size_t)LVQ_NUM_CLASSES * 8 + (size_t)B * kpad * 2;
+  size_t lds = (size_t)LVQ_NUM_CLASSES * 8 +
+               (x_chunk_major<B, M>() ? (size_t)B * (npad * 24 + 32) * 2 : (size_t)B * kpad * 2);
   if (M == kRot) {
     lds += ((size_t)cols * 4 + 15) & ~(size_t)15;
     if (ms.rot_q) lds += ((size_t)ms.rot_m * ms.rot_m * 4 + 255) & ~(size_t)255;
@@ -1183,44 +1153,27 @@ int launch_leech_mode(const MatSet& ms, int rows, int cols, const uint16_t* x, h
   }
   if (lds > device_lds_bytes()) return LVQ_E_SHAPE;
   const int cus = device_cus();
-  const int groups = (rows + R - 1) / R;  // items hold R rows each
-  const int threads = R > 1 ? 512 : wg_threads(groups, cus);
+  const int threads = wg_threads(rows, cus);
   const int wpb = threads / kWave;
   // as many workgroups as fit on the chip at once (one or two per CU, by
-  // registers and LDS), row groups grid-strided over their waves
+  // registers and LDS), rows grid-strided over their waves
   static OccupancyCache occupancy;  // this instantiation's own
-  const int occ = wgs_per_cu(occupancy, leech_gemv_kernel<B, BPL, M, D, R>, threads, lds);
-  long long wgs = ((long long)groups + wpb - 1) / wpb;
+  const int occ = wgs_per_cu(occupancy, leech_gemv_kernel<B, BPL, M, D>, threads, lds);
+  long long wgs = ((long long)rows + wpb - 1) / wpb;
   if (wgs > (long long)occ * cus) wgs = (long long)occ * cus;
   if (wgs < 1) wgs = 1;
   if (t_dry_run) {
-    *t_dry_run = {threads, (int)wgs, BPL, D, (int)lds, R};
+    *t_dry_run = {threads, (int)wgs, BPL, D, (int)lds};
     return LVQ_OK;
   }
   clear_hip_error();
-  hipLaunchKernelGGL((leech_gemv_kernel<B, BPL, M, D, R>), dim3((unsigned)wgs), dim3(threads), lds,
+  hipLaunchKernelGGL((leech_gemv_kernel<B, BPL, M, D>), dim3((unsigned)wgs), dim3(threads), lds,
                      st, ms, rows, nb, tau, cols, nchunks, (int)kpad, x);
   return launch_status();
 }
 
-// Rows per item.  At batch 3 and 4, with enough rows that pairs of rows
-// still give every SIMD four waves of 512-thread workgroups, an item holds
-// two rows at the same columns (each x read from LDS serves both) and a CU
-// runs two workgroups whose staging and decode phases overlap: 12288 x 4096
-// at batch 4 14.5 -> 13.2 us, at batch 3 12.1 -> 11.5.  At batch 2 the x
-// reads saved do not pay for the lost waves (9.6 -> 10.1 us), and with fewer
-// rows the pairs leave too few waves to hide the loads (4096 x 12288 at batch
-// 4: 12.7 -> 13.4 us); three rows per item lose everywhere.
-inline int rows_per_item(int B, int mode, int nb, int rows, int cus) {
-  return B >= 3 && (mode == kSingle || mode == kNoWeights) && (long long)rows >= 32LL * cus ? 2 : 1;
-}
-
 template <int B, int BPL, int M>
 int launch_leech_ring(const MatSet& ms, int rows, int cols, const uint16_t* x, hipStream_t st) {
-  if constexpr (B >= 3 && BPL == 1 && (M == kSingle || M == kNoWeights)) {
-    if (rows_per_item(B, M, cols / 24, rows, device_cus()) == 2)
-      return launch_leech_mode<B, BPL, M, 2, 2>(ms, rows, cols, x, st);
-  }
   if constexpr (BPL == 1 && M != kFused && M != kRot) {
     if (short_rows(M, cols / 24, rows)) return launch_leech_mode<B, BPL, M, 3>(ms, rows, cols, x, st);
   }
@@ -1471,7 +1424,7 @@ extern "C" int lvq_gemv_launch_info(int kind, int rows, int cols, int batch, int
   if (rows < 1 || cols < 24) return LVQ_E_SHAPE;
   static const int modes[] = {kSingle, kRot, kDirect, kOneHot, kLp2, kGain, kNoWeights};
   if (kind < 0 || kind >= (int)(sizeof(modes) / sizeof(modes[0]))) return LVQ_E_SHAPE;
-  LaunchInfo info = {0, 0, 0, 0, 0, 0};
+  LaunchInfo info = {0, 0, 0, 0, 0};
   t_dry_run = &info;
   const uintptr_t fake = (uintptr_t)1 << 30;
   const void* blob = (const void*)fake;
@@ -1491,6 +1444,5 @@ extern "C" int lvq_gemv_launch_info(int kind, int rows, int cols, int batch, int
   info_out[2] = info.blocks_per_lane;
   info_out[3] = info.ring;
   info_out[4] = info.lds_bytes;
-  info_out[5] = info.rows_per_item;
   return LVQ_OK;
 }

@@ -111,7 +111,7 @@ def test_leech_gemv_workloads(rows, cols, cfg, batch):
     (257, 129, 0, 4), (33, 200, 5, 1),
     (40, 600, 5, 2), (17, 1024, 0, 1), (300, 520, 3, 1),  # rows longer than one chunk
     (64, 682, 16, 4), (100, 2730, 16, 1),  # batch x cols at its limit, 65,536
-    (8193, 171, 5, 3), (8195, 130, 0, 4),  # two rows per item, an odd last row
+    (8193, 171, 5, 3), (8195, 130, 0, 4),  # many rows per wave at batch 3 and 4, odd counts
 ])
 def test_leech_gemv_ragged_and_full_ball(rows, nb, tau, batch):
     d = _all_class_matrix(rows, nb, tau, seed=rows * 1000 + nb)
