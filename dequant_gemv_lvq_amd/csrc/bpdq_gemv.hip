@@ -35,6 +35,15 @@ namespace lvq {
 constexpr int kBpdqRows = 16;
 constexpr int kBpdqUnit = 4;  // code words per lane unit: a quarter group
 
+// dot2(a, b, 0.f) as v_dot2_f32_f16 with an inline zero accumulator: the same
+// sum of two products; the compiler emits a move of 0 and the tied v_dot2c,
+// one instruction more for each of the 10 B accumulators of every quarter.
+__device__ __forceinline__ float dot2_first(uint32_t a, uint32_t b) {
+  float d;
+  asm("v_dot2_f32_f16 %0, %1, %2, 0" : "=v"(d) : "v"(a), "v"(b));
+  return d;
+}
+
 template <int B, int SLOTS>
 __global__ void __launch_bounds__(kBpdqRows * SLOTS)
 bpdq_gemv_kernel(const uint32_t* __restrict__ codes, const uint16_t* __restrict__ coeffs,
@@ -43,8 +52,14 @@ bpdq_gemv_kernel(const uint32_t* __restrict__ codes, const uint16_t* __restrict_
   constexpr int kThreads = kBpdqRows * SLOTS, kWaves = kThreads / kWave;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const int nwords = cols / 16, nunits = nwords / U;
-  uint32_t* xp = (uint32_t*)smem;                          // [B][nwords][8] pairs
-  float* xu = (float*)(xp + (size_t)B * nwords * 8);       // [B][nunits] unit sums
+  // x pairs [quarter][batch row][4 words][8 pairs] and quarter sums
+  // [quarter][batch row]: the batch stride is a constant, so the reads of a
+  // quarter take immediate offsets from one base.  Each quarter is padded by
+  // 8 words: a wave's four slots read four consecutive quarters, which
+  // unpadded would sit B x 512 bytes apart, on the same banks.
+  constexpr int kQS = B * U * 8 + 8;  // 32-bit words per quarter
+  uint32_t* xp = (uint32_t*)smem;
+  float* xu = (float*)(xp + (size_t)nunits * kQS);
   float* red = xu + (size_t)B * nunits;                    // [waves][16 rows][B]
 
   const int tid = threadIdx.x;
@@ -117,10 +132,14 @@ bpdq_gemv_kernel(const uint32_t* __restrict__ codes, const uint16_t* __restrict_
                dot2(b[3], kOnes, dot2(b[2], kOnes, 0.f)));
     s = dpp_add<0x4E, 0xF>(dpp_add<0xB1, 0xF>(s));  // quad_perm swaps: the quarter's 4 words
     if (i < nst) {
-      uint4* d = (uint4*)(xp + (size_t)i * 8);
+      int bb = 0;  // word i is word w of batch row bb
+#pragma unroll
+      for (int k = 1; k < B; ++k) bb += i >= k * nwords;
+      const int w = i - bb * nwords, q = w >> 2;
+      uint4* d = (uint4*)(xp + (size_t)q * kQS + (bb * U + (w & 3)) * 8);
       d[0] = make_uint4(p[0], p[1], p[2], p[3]);
       d[1] = make_uint4(p[4], p[5], p[6], p[7]);
-      if (i % U == 0) xu[i / U] = s;  // word i of batch row bb: quarter bb * nunits + w / 4
+      if ((w & 3) == 0) xu[q * B + bb] = s;
     }
   };
 #pragma unroll
@@ -144,11 +163,8 @@ bpdq_gemv_kernel(const uint32_t* __restrict__ codes, const uint16_t* __restrict_
 #pragma unroll
     for (int j = 0; j < U; ++j) w[j] = u[j];
     load_unit(n + SLOTS);  // the next unit, or nothing past the row
+    const uint32_t* xq = xp + (size_t)n * kQS;  // this quarter's pairs, batch row 0
     float a0[B][5], a1[B][5];
-#pragma unroll
-    for (int bb = 0; bb < B; ++bb)
-#pragma unroll
-      for (int e = 0; e < 5; ++e) a0[bb][e] = a1[bb][e] = 0.f;
 #pragma unroll
     for (int j = 0; j < U; ++j) {
       const uint32_t wj = w[j], w10 = wj >> 10;
@@ -165,14 +181,19 @@ bpdq_gemv_kernel(const uint32_t* __restrict__ codes, const uint16_t* __restrict_
       }
 #pragma unroll
       for (int bb = 0; bb < B; ++bb) {
-        const uint4* xw = (const uint4*)(xp + ((size_t)bb * nwords + U * n + j) * 8);
+        const uint4* xw = (const uint4*)(xq + (bb * U + j) * 8);
         const uint4 xa = xw[0], xb = xw[1];
         const uint32_t xv[8] = {xa.x, xa.y, xa.z, xa.w, xb.x, xb.y, xb.z, xb.w};
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
           const int e = c < 5 ? c : c - 5;  // columns 5..7 ride at the powers of 0..2
-          a0[bb][e] = dot2(m0[c], xv[c], a0[bb][e]);
-          a1[bb][e] = dot2(m1[c], xv[c], a1[bb][e]);
+          if (j == 0 && c < 5) {  // the accumulator's first term
+            a0[bb][e] = dot2_first(m0[c], xv[c]);
+            a1[bb][e] = dot2_first(m1[c], xv[c]);
+          } else {
+            a0[bb][e] = dot2(m0[c], xv[c], a0[bb][e]);
+            a1[bb][e] = dot2(m1[c], xv[c], a1[bb][e]);
+          }
         }
       }
     }
@@ -185,7 +206,7 @@ bpdq_gemv_kernel(const uint32_t* __restrict__ codes, const uint16_t* __restrict_
         s0 += a0[bb][e] * sc;
         s1 += a1[bb][e] * (sc * 0.5f);
       }
-      acc[bb] += c0 * s0 + c1 * s1 + c2 * xu[bb * nunits + n];
+      acc[bb] += c0 * s0 + c1 * s1 + c2 * xu[n * B + bb];
     }
   }
 
@@ -213,7 +234,8 @@ template <int B, int SLOTS>
 int launch_bpdq(const uint32_t* codes, const uint16_t* coeffs, int rows, int cols,
                 const uint16_t* x, float* y, hipStream_t st) {
   constexpr int kThreads = kBpdqRows * SLOTS;
-  const size_t lds = (size_t)B * cols * 2 + (size_t)B * (cols / (16 * kBpdqUnit)) * 4 +
+  const size_t quarters = cols / (16 * kBpdqUnit);
+  const size_t lds = quarters * (B * kBpdqUnit * 8 + 8) * 4 + quarters * B * 4 +
                      (size_t)(kThreads / kWave) * kBpdqRows * B * 4;
   if (lds > device_lds_bytes()) return LVQ_E_SHAPE;
   const int ntiles = (rows + kBpdqRows - 1) / kBpdqRows;
