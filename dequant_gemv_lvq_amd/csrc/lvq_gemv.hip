@@ -56,20 +56,25 @@ inline int wg_threads(int rows, int cus) {
 }
 
 // Blocks per lane for rows of nb blocks.  First the fewest idle lane slots in
-// a row's last chunk; among those the largest (fewest items, least per-item
-// work) unless there are three to five waves per SIMD, where the one giving
-// each wave closest to four items wins (enough loads in flight behind the
-// decode).  Measured on MI355X over the shapes of a Qwen3-8B layer.
-inline int choose_bpl(int nb, int maxb, int rows, int cus) {
+// a row's last chunk; among those the one giving each wave closest to four
+// items (enough loads in flight behind the decode; ties to the larger), or
+// with two or fewer waves per SIMD the largest (fewest items, least per-item
+// work).  Measured on MI355X over the shapes of a Qwen3-8B layer and the
+// same bytes as 2048 x 24576 .. 32768 x 1536: with six or more waves per SIMD
+// the largest blocks per lane (one item per wave) were up to 1.3 us slower
+// (8192 x 6144: 8.8 against 7.6 us).  The fused multi-matrix launch, whose
+// items each pick their matrix, keeps the largest there too (its q/k/v set,
+// 6144 rows at 4096 columns: the stack's 144 launches 1321 us, 1376 with
+// more, smaller items).
+inline int choose_bpl(int nb, int maxb, int rows, int cus, bool fused) {
   const int wpb = wg_threads(rows, cus) / kWave;
   long long waves = ((long long)rows + wpb - 1) / wpb;
   if (waves > 2LL * cus) waves = 2LL * cus;  // up to two workgroups per CU
   waves *= wpb;
   const long long rows_per_wave = ((long long)rows + waves - 1) / waves;
   // with two or fewer waves per SIMD an item's loads cannot hide behind
-  // another wave's decode anyway, and with six or more they always can: in
-  // both cases fewer, larger items win
-  const bool largest = waves >= 6LL * 4 * cus || waves <= 2LL * 4 * cus;
+  // another wave's decode anyway: fewer, larger items win
+  const bool largest = waves <= 2LL * 4 * cus || (fused && waves >= 6LL * 4 * cus);
   long long best_idle = -1;
   for (int b = 1; b <= maxb; ++b) {
     const long long per = (long long)kWave * b;
@@ -180,15 +185,16 @@ constexpr int kMaxFused = 4;
 // epilogue
 constexpr int kSingle = 0, kFused = 1, kNoWeights = 2, kGain = 3, kLp2 = 4, kRot = 5,
               kDirect = 6, kOneHot = 7, kLp2x = 8;
-// Rows of two or three 64-block chunks (64 < nb <= 192, K <= 4608) with rows
-// to fill the chip: one block per lane and a ring of three register sets, so
-// that a row is in flight whole (measured on MI355X: 4096 x 4096 batch 1 5.08
-// -> 4.72 us, 12288 x 4096 8.79 -> 8.37 us; more items in flight on longer
-// rows was slower at every depth tried).  Single-matrix launches only: the
-// fused multi-matrix launch (per-item matrix selection) and the rotating one
-// (its prologue) measured slower with it.
+// Rows of three 64-block chunks (128 < nb <= 192 blocks) with
+// rows to fill the chip: one block per lane and a ring of three register
+// sets, so that a row is in flight whole (measured on MI355X: 4096 x 4096
+// batch 1 5.08 -> 4.72 us, 12288 x 4096 8.79 -> 8.37 us; more items in flight
+// on longer rows was slower at every depth tried, and on rows of two chunks
+// too: 16384 x 3072 7.97 us with a ring of two, 8.52 with three).
+// Single-matrix launches only: the fused multi-matrix launch (per-item matrix
+// selection) and the rotating one (its prologue) measured slower with it.
 inline bool short_rows(int mode, int nb, int rows) {
-  return mode != kFused && mode != kRot && nb > 64 && nb <= 3 * 64 && rows >= 2048;
+  return mode != kFused && mode != kRot && nb > 2 * 64 && nb <= 3 * 64 && rows >= 2048;
 }
 
 constexpr bool is_lp2(int M) { return M == kLp2 || M == kLp2x; }
@@ -1230,7 +1236,7 @@ int launch_leech(const MatSet& ms, int n, int mode, int rows, int cols, const ui
   const int bpl = short_rows(mode, nb, rows)
                       ? 1
                       : choose_bpl(nb, (mode == kGain || mode == kRot) && B >= 2 ? 3 : max_bpl(B),
-                                   rows, device_cus());
+                                   rows, device_cus(), mode == kFused);
   if constexpr (max_bpl(B) >= 4) {
     if (bpl == 4) {
       const int e = launch_leech_bpl<B, 4>(ms, mode, rows, cols, x, st);

@@ -568,3 +568,10 @@ def test_launch_info_rules_and_validation():
     # the fused rotation and few rows keep the blocks-per-lane rule
     assert lvq.gemv_launch_info("rotated", 12288, 4096)["ring"] == 2
     assert lvq.gemv_launch_info("gemv", 1024, 4096)["ring"] == 2
+    # many waves per SIMD: the blocks per lane that give each wave about four
+    # items, not one item per wave; rows of two chunks keep the ring of two
+    for rows, cols in ((8192, 6144), (16384, 3072), (32768, 1536)):
+        info = lvq.gemv_launch_info("gemv", rows, cols)
+        assert (info["blocks_per_lane"], info["ring"]) == (1, 2), (rows, cols)
+    wide = lvq.gemv_launch_info("gemv", 2048, 24576)  # two waves per SIMD: largest
+    assert wide["blocks_per_lane"] == 4
