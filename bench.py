@@ -124,25 +124,36 @@ class Timed:
     """`trials` runs of `steps` back-to-back launches fn(i) on the current
     stream, each bracketed by events on that stream.  A bounded spin kernel
     (torch.cuda._sleep) holds the GPU while a trial is enqueued, so host
-    submission never shows on the GPU timeline."""
+    submission never shows on the GPU timeline.  That is checked: if the GPU
+    has already passed the trial's start event when the last launch has been
+    enqueued, the spin ended first and the GPU may have waited for the host,
+    so the trial is run again with twice the hold (at most `retries` times;
+    `redone` counts these over the process)."""
 
     cycles_per_ms = None
+    redone = 0
 
-    def __init__(self, torch, fn, steps, warmup, trials, enqueue_ms=0.04):
+    def __init__(self, torch, fn, steps, warmup, trials, enqueue_ms=0.04, retries=3):
         for i in range(warmup):
             fn(i)
         torch.cuda.synchronize()
         st = torch.cuda.current_stream()
-        hold = self._hold_cycles(torch, 2.0 + steps * enqueue_ms)
+        hold_ms = 2.0 + steps * enqueue_ms
         per = []
         for t in range(trials):
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            torch.cuda._sleep(hold)
-            a.record(st)
-            for i in range(steps):
-                fn(t * steps + i)
-            b.record(st)
-            torch.cuda.synchronize()
+            for attempt in range(retries + 1):
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                torch.cuda._sleep(self._hold_cycles(torch, hold_ms))
+                a.record(st)
+                for i in range(steps):
+                    fn(t * steps + i)
+                b.record(st)
+                drained = a.query()  # the spin ended before the enqueue did
+                torch.cuda.synchronize()
+                if not drained or attempt == retries:
+                    break
+                Timed.redone += 1
+                hold_ms *= 2
             per.append(a.elapsed_time(b) * 1e3 / steps)
         per.sort()
         self.us = per
@@ -963,7 +974,8 @@ def ceiling_sweep(torch, lvq, args, nbytes):
                                  "us_min": round(tm.us[0], 3)})
                     log("read %4d thr %d/CU u%d nt%d: %.3f us" % (threads, wpc, unroll, nt,
                                                                  tm.median))
-    floor = timed(lambda i: lvq.stream_read_geom(buf[0], 0, sink, 256, 1, 1, 1)).median
+    tfl = timed(lambda i: lvq.stream_read_geom(buf[0], 0, sink, 256, 1, 1, 1))
+    floor = tfl.median
     base = timed(lambda i: lvq.stream_read(buf[i % n], nb4, sink[:lvq.STREAM_SINK_WORDS])).median
     dst = torch.empty((2, stride), dtype=torch.uint8, device="cuda")
     cp = timed(lambda i: dst[i % 2].copy_(buf[i % n])).median
@@ -972,6 +984,7 @@ def ceiling_sweep(torch, lvq, args, nbytes):
            "trials": args.trials, "sweep": rows, "best": best,
            "best_gbps": round(nbytes / (best["us"] * 1e-6) / 1e9, 1),
            "lvq_stream_read_us": round(base, 3), "launch_floor_us": round(floor, 3),
+           "launch_floor_us_min": round(tfl.us[0], 3), "timing_trials_redone": Timed.redone,
            "d2d_copy_us": round(cp, 3),
            "d2d_copy_gbps_read_plus_write": round(2 * nbytes / (cp * 1e-6) / 1e9, 1)}
     log("ceiling over %d B: best %.3f us (%s), lvq_stream_read %.3f us, d2d copy %.3f us, "
@@ -1188,6 +1201,7 @@ def run(torch, lvq, args, props, arch, B, leg, pool, stack_results, stack_jobs):
         "pct_stream_ceiling": head["pct_stream_ceiling"],
         "cpu_cores_used": cpu["cores"] if cpu else None,
         "cpu_cores_available": cpu["cores_available"] if cpu else None,
+        "timing_trials_redone": Timed.redone,
         "parity_checks": len(leg.ratios),
         "parity_max_ratio_all_records": leg.worst(),
         "bitexact": head.get("bitexact"),

@@ -38,6 +38,29 @@ int device_cus();
 // Largest dynamic LDS allocation a workgroup may request on the current device.
 size_t device_lds_bytes();
 
+constexpr int kMaxDevices = 64;
+
+// Workgroups per CU (at most 2) that fit at once for one kernel, by the occupancy query,
+// kept in that kernel's own cache (`cache`, one per kernel instantiation) per
+// device and per (workgroup size, LDS above 64 KiB).  The entries are ints
+// written whole with the same value by any thread that races on them.
+typedef int OccupancyCache[kMaxDevices][3][2];
+template <typename K>
+int wgs_per_cu(OccupancyCache& cache, K kernel, int threads, size_t lds) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) dev = 0;
+  const int ti = threads == 1024 ? 0 : threads == 512 ? 1 : 2, li = lds > 64 * 1024;
+  int n = __atomic_load_n(&cache[dev][ti][li], __ATOMIC_RELAXED);
+  if (!n) {
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, threads, lds) != hipSuccess ||
+        n < 1)
+      n = 1;
+    n = n > 2 ? 2 : n;
+    __atomic_store_n(&cache[dev][ti][li], n, __ATOMIC_RELAXED);
+  }
+  return n;
+}
+
 // ---------------------------------------------------------------- device side
 
 template <int CTRL, int ROW_MASK>

@@ -164,17 +164,10 @@ int launch_fp16(const uint16_t* W, int rows, int cols, const uint16_t* x, float*
   int threads = kDenseThreads;
   while (threads > 256 && rows < cus * (threads / kWave)) threads /= 2;
   const int wpb = threads / kWave;
-  static int occupancy[3][2] = {{0, 0}, {0, 0}, {0, 0}};
-  const int ti = threads == 1024 ? 0 : threads == 512 ? 1 : 2, li = lds > 64 * 1024;
-  if (!occupancy[ti][li]) {
-    int n = 1;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fp16_gemv_kernel<B>, threads, lds) !=
-            hipSuccess || n < 1)
-      n = 1;
-    occupancy[ti][li] = n > 2 ? 2 : n;
-  }
+  static OccupancyCache occupancy;  // this instantiation's own
+  const int occ = wgs_per_cu(occupancy, fp16_gemv_kernel<B>, threads, lds);
   long long wgs = ((long long)rows + wpb - 1) / wpb;
-  if (wgs > (long long)occupancy[ti][li] * cus) wgs = (long long)occupancy[ti][li] * cus;
+  if (wgs > (long long)occ * cus) wgs = (long long)occ * cus;
   if (wgs < 1) wgs = 1;
   clear_hip_error();
   hipLaunchKernelGGL(fp16_gemv_kernel<B>, dim3((unsigned)wgs), dim3(threads), lds, st, W, rows,

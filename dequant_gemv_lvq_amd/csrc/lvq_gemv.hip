@@ -44,7 +44,6 @@ constexpr int kMaxWgThreads = 1024;
 // blocks per lane per work item: the code words of the current and the next
 // item must stay in registers (no spills) next to B accumulator pairs
 constexpr int max_bpl(int B) { return B <= 2 ? 4 : 2; }
-constexpr int kMaxDevices = 64;
 
 // Workgroup size for `rows` rows: 1024 threads (x staged once per 16 waves)
 // when there are rows for 16 waves on every CU, smaller otherwise so the rows
@@ -1115,11 +1114,6 @@ int zero_output(float* y, size_t n, hipStream_t st) {
   return launch_status();
 }
 
-// Workgroups per CU that fit at once for one kernel, by the occupancy query,
-// kept in that kernel's own cache (`cache`, one per kernel instantiation) per
-// device and per (workgroup size, LDS above 64 KiB).  The entries are ints
-// written whole with the same value by any thread that races on them.
-typedef int OccupancyCache[kMaxDevices][3][2];
 
 // When set (lvq_gemv_launch_info), the Leech launch path records the launch
 // it would make here instead of making it.
@@ -1127,21 +1121,6 @@ struct LaunchInfo {
   int threads, workgroups, blocks_per_lane, ring, lds_bytes;
 };
 thread_local LaunchInfo* t_dry_run = nullptr;
-template <typename K>
-int wgs_per_cu(OccupancyCache& cache, K kernel, int threads, size_t lds) {
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) dev = 0;
-  const int ti = threads == 1024 ? 0 : threads == 512 ? 1 : 2, li = lds > 64 * 1024;
-  int n = __atomic_load_n(&cache[dev][ti][li], __ATOMIC_RELAXED);
-  if (!n) {
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, threads, lds) != hipSuccess ||
-        n < 1)
-      n = 1;
-    n = n > 2 ? 2 : n;
-    __atomic_store_n(&cache[dev][ti][li], n, __ATOMIC_RELAXED);
-  }
-  return n;
-}
 
 template <int B, int BPL, int M, int D>
 int launch_leech_mode(const MatSet& ms, int rows, int cols, const uint16_t* x, hipStream_t st) {

@@ -81,12 +81,12 @@ unfold_kernel(const uint64_t* __restrict__ words, size_t n, int8_t* __restrict__
 
 namespace {
 std::mutex g_upload_mu;
-bool g_uploaded[64] = {};
+bool g_uploaded[kMaxDevices] = {};
 }  // namespace
 
 int upload_index_tables() {
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return LVQ_E_HIP;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return LVQ_E_HIP;
   std::lock_guard<std::mutex> lock(g_upload_mu);
   if (g_uploaded[dev]) return LVQ_OK;
   const IndexTables& T = index_tables();
