@@ -127,8 +127,11 @@ class Timed:
     submission never shows on the GPU timeline.  That is checked: if the GPU
     has already passed the trial's start event when the last launch has been
     enqueued, the spin ended first and the GPU may have waited for the host,
-    so the trial is run again with twice the hold (at most `retries` times;
-    `redone` counts these over the process)."""
+    so the trial is run again with twice the hold (at most `retries` times,
+    the hold at most 2^retries times the first; `redone` counts these over
+    the process).  Trials of more than about a thousand launches (the stack
+    records) cannot pass the check: the host's enqueue then blocks until the
+    GPU has completed earlier launches, so they run with retries=0."""
 
     cycles_per_ms = None
     redone = 0
@@ -139,6 +142,7 @@ class Timed:
         torch.cuda.synchronize()
         st = torch.cuda.current_stream()
         hold_ms = 2.0 + steps * enqueue_ms
+        max_hold_ms = hold_ms * (1 << retries)
         per = []
         for t in range(trials):
             for attempt in range(retries + 1):
@@ -153,7 +157,7 @@ class Timed:
                 if not drained or attempt == retries:
                     break
                 Timed.redone += 1
-                hold_ms *= 2
+                hold_ms = min(2 * hold_ms, max_hold_ms)
             per.append(a.elapsed_time(b) * 1e3 / steps)
         per.sort()
         self.us = per
@@ -849,11 +853,14 @@ class Bench:
 
         # host enqueue time per pass: ~252 launches (GEMV only), ~1000 with the
         # renormalisation ops; the hold covers it
-        tm = Timed(torch, gemv_only, 5, 2, self.args.trials, enqueue_ms=len(order) * 0.02)
-        tf = Timed(torch, fused_only, 5, 2, self.args.trials, enqueue_ms=len(groups) * 0.08)
-        t0 = Timed(torch, noweights_only, 5, 2, self.args.trials, enqueue_ms=len(order) * 0.02)
+        tm = Timed(torch, gemv_only, 5, 2, self.args.trials, enqueue_ms=len(order) * 0.02,
+                   retries=0)
+        tf = Timed(torch, fused_only, 5, 2, self.args.trials, enqueue_ms=len(groups) * 0.08,
+                   retries=0)
+        t0 = Timed(torch, noweights_only, 5, 2, self.args.trials, enqueue_ms=len(order) * 0.02,
+                   retries=0)
         tc = Timed(torch, lambda _: chain(False), 3, 1, self.args.trials,
-                   enqueue_ms=len(order) * 0.08)
+                   enqueue_ms=len(order) * 0.08, retries=0)
         us = tm.median  # µs per pass over all GEMVs
         rec = {
             "arm": "leech", "cfg": 5, "model": "Qwen3-8B-shaped Leech stack, random init",

@@ -80,3 +80,18 @@ def test_retries_are_bounded(fake_torch):
     assert bench.Timed.redone == 2
     assert t.us == [7.0 * 1e3 / 4]  # the last attempt is kept
     assert len(cuda.holds) == 3
+
+
+def test_the_hold_is_capped_across_trials(fake_torch):
+    # a trial that never passes the check (the host blocks until the GPU
+    # has drained) must not make later holds grow without bound
+    torch, cuda = fake_torch([True] * 6, [1.0, 1.0])
+    bench.Timed(torch, lambda i: None, steps=4, warmup=0, trials=2, retries=2)
+    h = 1000.0 * (2.0 + 4 * 0.04)
+    assert cuda.holds == [h, 2 * h, 4 * h, 4 * h, 4 * h, 4 * h]
+
+
+def test_no_retries_keeps_every_first_attempt(fake_torch):
+    torch, cuda = fake_torch([True, True], [1.0, 2.0])
+    t = bench.Timed(torch, lambda i: None, steps=5, warmup=0, trials=2, retries=0)
+    assert bench.Timed.redone == 0 and t.us == [200.0, 400.0] and len(cuda.holds) == 2
