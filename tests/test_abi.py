@@ -143,6 +143,9 @@ def test_device_entry_points_validate_before_launch():
     assert lib.bpdq_gemv(A, A, 16, 100, A, A, 1, None) == lvq.LVQ_E_SHAPE
     assert lib.bpdq_gemv(A, A, 16, 256, A, A, 9, None) == lvq.LVQ_E_BATCH
     assert lib.bpdq_gemv(A, None, 16, 256, A, A, 1, None) == lvq.LVQ_E_NULL
+    assert lib.bpdq_gemv(A, A, 16, 65536 + 256, A, A, 1, None) == lvq.LVQ_E_SHAPE  # batch x cols
+    assert lib.bpdq_gemv(A, A, 16, 16384 + 256, A, A, 4, None) == lvq.LVQ_E_SHAPE
+    assert lib.bpdq_gemv(A, A, 1 << 20, 16384, A, A, 1, None) == lvq.LVQ_E_SHAPE  # codes > 2 GiB
     assert lib.trellis_gemv(A, A, A, 16, 300, A, A, 1, None) == lvq.LVQ_E_SHAPE
     assert lib.trellis_gemv(A, A, A, 16, 4096, A, A, 4, None) == lvq.LVQ_E_SHAPE
     assert lib.trellis_gemv(A, A, A + 2, 16, 256, A, A, 1, None) == lvq.LVQ_E_ALIGN
