@@ -92,3 +92,28 @@ def test_fp16_random_shapes(case):
     r = og.check(to_host(yd, np.float32), y64, bound)
     _report("fp16 %s" % _ids(case), r)
     assert r <= 1.0
+
+
+# ---------------------------------------------------------------- the largest widths
+
+@pytest.mark.parametrize("kind,rows,cols,batch", [
+    ("bpdq", 16, 63488, 1),   # the widest that fits LDS at batch 1
+    ("bpdq", 16, 32768, 2), ("bpdq", 17, 21760, 3), ("bpdq", 32, 16384, 4),  # batch x cols
+    ("trellis", 16, 6144, 2), ("trellis", 3, 12288, 1),
+    ("fp16", 16, 65536, 1), ("fp16", 5, 16384, 4),
+])
+def test_arms_at_their_largest_widths(kind, rows, cols, batch):
+    case = (99, rows, cols, batch)
+    {"bpdq": test_bpdq_random_shapes, "trellis": test_trellis_random_shapes,
+     "fp16": test_fp16_random_shapes}[kind](case)
+
+
+def test_bpdq_past_the_lds_is_refused():
+    # 63,744 columns at batch 1 pass the batch x cols bound but not the LDS
+    rows, cols = 16, 63744
+    d = synth.bpdq_matrix(rows, cols)
+    x = synth.activations(cols, 1, 2)
+    yd = empty((1, rows), np.float32)
+    with pytest.raises(lvq.LvqError) as e:
+        lvq.bpdq_gemv(to_dev(d["codes"]), to_dev(d["coeffs"]), rows, cols, to_dev(x), yd, 1)
+    assert e.value.code == lvq.LVQ_E_SHAPE
